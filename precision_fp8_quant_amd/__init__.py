@@ -1,0 +1,198 @@
+"""Python binding of the fp8q C ABI (include/fp8q.h) for AMD MI355X.
+
+Argument marshalling only: every step of quantization and GEMM runs in the
+HIP kernels of ``libfp8q.so``.  torch supplies device memory and the stream.
+Importing this package fails loudly if the library has not been built
+(``python -c "import __graft_entry__; __graft_entry__.build()"``); there is
+no CPU fallback.
+
+Functions keep the C names:
+    fp8_quant_tile(x, tile, mode)              -> (q, scales)
+    fp8_quant_block(w, mode, transposed)       -> (q, scales[, q_t, scales_t])
+    fp8_gemm_blockscaled(kind, a, sa, b, sb)   -> c
+    fp8_gemm_blockscaled_grouped(gmap, a, sa, b, sb) -> c
+FP8 tensors are torch.uint8 holding OCP E4M3FN codes.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libfp8q.so")
+
+# enums of include/fp8q.h
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_ALIAS, ERR_HIP, ERR_ARG = range(8)
+BF16, F32 = 0, 1
+MAXABS, POW2 = 0, 1
+TILE_1x128, TILE_128x1 = 0, 1
+FPROP, DGRAD, WGRAD = 0, 1, 2
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_int = ctypes.c_int
+_ptr = ctypes.c_void_p
+
+# (name, argtypes) for every entry point of include/fp8q.h
+SIGNATURES = {
+    "fp8_quant_tile": [_ptr, _int, _i64, _i64, _i64, _int, _int, _ptr, _i64, _ptr, _ptr],
+    "fp8_quant_block": [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr],
+    "fp8_gemm_blockscaled": [_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _int, _i64,
+                             _int, _ptr],
+    "fp8_gemm_blockscaled_grouped": [_i32, _i64, _i64, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _int,
+                                     _i64, _ptr],
+    "fp8q_status_string": [_int],
+    "fp8q_abi_version": [],
+}
+
+
+class Fp8qError(RuntimeError):
+    """A non-OK status returned by the C ABI."""
+
+    def __init__(self, status):
+        self.status = status
+        super().__init__(status_string(status))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, argtypes in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_char_p if name == "fp8q_status_string" else ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status):
+    return lib.fp8q_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != OK:
+        raise Fp8qError(status)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _codes(t):
+    """Accept uint8 or float8_e4m3fn code tensors; return the uint8 view."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"FP8 operands are uint8 E4M3FN codes, got {t.dtype}")
+    return t
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D row-major tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t
+
+
+def _ld(t):
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def fp8_quant_tile(x, tile=TILE_1x128, mode=MAXABS, q=None, scales=None, stream=None):
+    """1x128 (q[rows][cols], scales[cols/128][rows]) or 128x1 (q[cols][rows] transposed,
+    scales[rows/128][cols]) quantization of a 2-D bf16/fp32 tensor."""
+    _rowmajor(x, "x")
+    rows, cols = x.shape
+    if q is None:
+        shape = (rows, cols) if tile == TILE_1x128 else (cols, rows)
+        q = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        shape = (cols // 128, rows) if tile == TILE_1x128 else (rows // 128, cols)
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    q = _codes(q)
+    _check(lib.fp8_quant_tile(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), tile, mode,
+                              q.data_ptr(), _ld(q), scales.data_ptr(), _stream(stream)))
+    return q, scales
+
+
+def fp8_quant_block(w, mode=MAXABS, transposed=False, q=None, scales=None, q_t=None, scales_t=None,
+                    stream=None):
+    """128x128 block quantization; with transposed=True also the transposed codes
+    q_t[cols][rows] and scales_t[cols/128][rows/128] (Dgrad's weight operand)."""
+    _rowmajor(w, "w")
+    rows, cols = w.shape
+    dev = w.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=dev)
+    if transposed:
+        if q_t is None:
+            q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        if scales_t is None:
+            scales_t = torch.empty((cols // 128, rows // 128), dtype=torch.float32, device=dev)
+    q = _codes(q)
+    qt_ptr = _codes(q_t).data_ptr() if q_t is not None else None
+    ld_qt = _ld(q_t) if q_t is not None else 0
+    st_ptr = scales_t.data_ptr() if scales_t is not None else None
+    _check(lib.fp8_quant_block(w.data_ptr(), _dtype_code(w), rows, cols, _ld(w), mode,
+                               q.data_ptr(), _ld(q), scales.data_ptr(), qt_ptr, ld_qt, st_ptr,
+                               _stream(stream)))
+    if transposed:
+        return q, scales, q_t, scales_t
+    return q, scales
+
+
+def fp8_gemm_blockscaled(kind, a, a_scales, b, b_scales, out_dtype=torch.bfloat16, c=None,
+                         accumulate=False, stream=None):
+    """C[M][N] (+)= A . B^T with per-128-K-group scales (see include/fp8q.h)."""
+    a, b = _codes(_rowmajor(a, "a")), _codes(_rowmajor(b, "b"))
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError("a and b disagree on K")
+    if c is None:
+        c = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _rowmajor(c, "c")
+    _check(lib.fp8_gemm_blockscaled(kind, m, n, k, a.data_ptr(), _ld(a), a_scales.data_ptr(),
+                                    b.data_ptr(), _ld(b), b_scales.data_ptr(), c.data_ptr(),
+                                    _dtype_code(c), _ld(c), 1 if accumulate else 0, _stream(stream)))
+    return c
+
+
+def fp8_gemm_blockscaled_grouped(group_of_mtile, a, a_scales, b, b_scales, out_dtype=torch.bfloat16,
+                                 c=None, stream=None):
+    """Grouped Fprop: b is [G][N][K] codes, b_scales [G][N/128][K/128], group_of_mtile int32
+    [M_total/128] on the device."""
+    a = _codes(_rowmajor(a, "a"))
+    b = _codes(b)
+    if b.dim() != 3 or not b.is_contiguous():
+        raise ValueError("b must be a contiguous [G][N][K] tensor")
+    g, n, k = b.shape
+    m = a.shape[0]
+    if a.shape[1] != k:
+        raise ValueError("a and b disagree on K")
+    if group_of_mtile.dtype != torch.int32 or not group_of_mtile.is_cuda:
+        raise ValueError("group_of_mtile must be a device int32 tensor")
+    if c is None:
+        c = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _check(lib.fp8_gemm_blockscaled_grouped(g, m, n, k, group_of_mtile.data_ptr(), a.data_ptr(), _ld(a),
+                                            a_scales.data_ptr(), b.data_ptr(), b_scales.data_ptr(),
+                                            c.data_ptr(), _dtype_code(c), _ld(c), _stream(stream)))
+    return c

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every entry point declared in include/fp8q.h,
+and rejects bad arguments before anything is launched (CPU only: no call here
+reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+fp8q = pytest.importorskip("precision_fp8_quant_amd", reason="libfp8q.so not built")
+
+A = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced,
+B = 0x20000000       # because every call below fails validation first
+C = 0x40000000
+D = 0x60000000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert names == {"fp8_quant_tile", "fp8_quant_block", "fp8_gemm_blockscaled",
+                     "fp8_gemm_blockscaled_grouped", "fp8q_status_string", "fp8q_abi_version"}
+    raw = ctypes.CDLL(fp8q.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(fp8q.SIGNATURES) == names
+
+
+def test_version_and_status_strings():
+    assert fp8q.lib.fp8q_abi_version() == 100
+    for s in range(8):
+        assert fp8q.status_string(s).startswith("FP8Q_")
+    assert fp8q.status_string(99) == "unknown fp8q status"
+
+
+def _tile(**kw):
+    args = dict(x=A, dt=fp8q.BF16, rows=128, cols=256, ldx=256, tile=fp8q.TILE_1x128, mode=fp8q.MAXABS,
+                q=B, ldq=256, s=C)
+    args.update(kw)
+    return fp8q.lib.fp8_quant_tile(args["x"], args["dt"], args["rows"], args["cols"], args["ldx"], args["tile"],
+                                   args["mode"], args["q"], args["ldq"], args["s"], None)
+
+
+def test_quant_tile_validation():
+    assert _tile(rows=0) == fp8q.OK and _tile(cols=0, x=None) == fp8q.OK   # empty: no-op
+    assert _tile(dt=7) == fp8q.ERR_ARG
+    assert _tile(tile=5) == fp8q.ERR_ARG
+    assert _tile(mode=2) == fp8q.ERR_ARG
+    assert _tile(rows=-1) == fp8q.ERR_SHAPE
+    assert _tile(x=None) == fp8q.ERR_NULL
+    assert _tile(s=None) == fp8q.ERR_NULL
+    assert _tile(ldx=128) == fp8q.ERR_SHAPE
+    assert _tile(x=A + 2) == fp8q.ERR_ALIGN
+    assert _tile(ldx=260) == fp8q.ERR_ALIGN          # 520 bytes is not a multiple of 16
+    assert _tile(cols=200, ldx=200, ldq=208) == fp8q.ERR_UNSUPPORTED
+    assert _tile(tile=fp8q.TILE_128x1, rows=100, ldq=256) == fp8q.ERR_UNSUPPORTED
+    assert _tile(tile=fp8q.TILE_128x1, cols=252, ldx=256, ldq=128) == fp8q.ERR_UNSUPPORTED
+    assert _tile(q=A + 64) == fp8q.ERR_ALIAS         # codes overlap the input
+    assert _tile(s=B + 1024) == fp8q.ERR_ALIAS       # scales overlap the codes
+
+
+def _block(**kw):
+    args = dict(w=A, dt=fp8q.F32, rows=256, cols=384, ldw=384, mode=fp8q.POW2, q=B, ldq=384, s=C,
+                qt=None, ldqt=0, st=None)
+    args.update(kw)
+    return fp8q.lib.fp8_quant_block(args["w"], args["dt"], args["rows"], args["cols"], args["ldw"], args["mode"],
+                                    args["q"], args["ldq"], args["s"], args["qt"], args["ldqt"], args["st"],
+                                    None)
+
+
+def test_quant_block_validation():
+    assert _block(rows=0, w=None) == fp8q.OK
+    assert _block(mode=9) == fp8q.ERR_ARG
+    assert _block(q=None) == fp8q.ERR_NULL
+    assert _block(qt=D, ldqt=256) == fp8q.ERR_NULL             # q_t without scales_t
+    assert _block(qt=D, ldqt=128, st=D + 0x100000) == fp8q.ERR_SHAPE
+    assert _block(rows=200) == fp8q.ERR_UNSUPPORTED
+    assert _block(ldq=392) == fp8q.ERR_ALIGN
+    assert _block(qt=B + 16, ldqt=256, st=D) == fp8q.ERR_ALIAS  # transposed codes overlap codes
+
+
+def _gemm(**kw):
+    args = dict(kind=fp8q.FPROP, M=256, N=256, K=512, a=A, lda=512, sa=B, b=C, ldb=512, sb=D,
+                c=0x7000000, cdt=fp8q.BF16, ldc=256, acc=0)
+    args.update(kw)
+    return fp8q.lib.fp8_gemm_blockscaled(args["kind"], args["M"], args["N"], args["K"], args["a"], args["lda"],
+                                         args["sa"], args["b"], args["ldb"], args["sb"], args["c"], args["cdt"],
+                                         args["ldc"], args["acc"], None)
+
+
+def test_gemm_validation():
+    assert _gemm(M=0) == fp8q.OK
+    assert _gemm(kind=3) == fp8q.ERR_ARG
+    assert _gemm(cdt=4) == fp8q.ERR_ARG
+    assert _gemm(acc=2) == fp8q.ERR_ARG
+    assert _gemm(K=-128) == fp8q.ERR_SHAPE
+    assert _gemm(c=None) == fp8q.ERR_NULL
+    assert _gemm(sb=None) == fp8q.ERR_NULL
+    assert _gemm(lda=256) == fp8q.ERR_SHAPE
+    assert _gemm(ldc=200) == fp8q.ERR_SHAPE
+    assert _gemm(b=C + 8) == fp8q.ERR_ALIGN
+    assert _gemm(M=200) == fp8q.ERR_UNSUPPORTED
+    assert _gemm(acc=1) == fp8q.ERR_UNSUPPORTED                  # accumulate needs FP32 output
+    assert _gemm(c=A + 4096) == fp8q.ERR_ALIAS
+
+
+def _grouped(**kw):
+    args = dict(G=4, M=512, N=256, K=256, gmap=0x9000000, a=A, lda=256, sa=B, b=C, sb=D, c=0x7000000,
+                cdt=fp8q.BF16, ldc=256)
+    args.update(kw)
+    return fp8q.lib.fp8_gemm_blockscaled_grouped(args["G"], args["M"], args["N"], args["K"], args["gmap"], args["a"],
+                                                 args["lda"], args["sa"], args["b"], args["sb"], args["c"],
+                                                 args["cdt"], args["ldc"], None)
+
+
+def test_grouped_validation():
+    assert _grouped(M=0) == fp8q.OK
+    assert _grouped(G=0) == fp8q.ERR_SHAPE
+    assert _grouped(gmap=None) == fp8q.ERR_NULL
+    assert _grouped(gmap=0x9000002) == fp8q.ERR_ALIGN
+    assert _grouped(N=192) == fp8q.ERR_UNSUPPORTED
+    assert _grouped(c=C + 0x100) == fp8q.ERR_ALIAS
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(fp8q.Fp8qError):
+        fp8q._check(fp8q.ERR_SHAPE)

@@ -1,0 +1,220 @@
+"""GPU parity of the HIP quantizers against the CPU oracle: bit-exact FP8 bytes
+and FP32 scales, through the C ABI.
+
+Small cases cover several tiles and a ragged tail; edge cases sweep every
+BF16 value in range and every float32 value around each E4M3 rounding
+midpoint through the hardware converter; the full-size cases run the
+quantizer-only workload (activation 8192x7168, weight 18432x7168) and the
+Dgrad/Wgrad operands at their real shapes and check sampled rows/columns that
+the oracle recomputes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import e4m3, quant as oq
+from tests.helpers import assert_bytes_equal, dev, dev_bf16, host, require_gpu
+from workloads import add_outliers, linear_layer, normal_f32, output_grad, to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+MODES = [("maxabs", 0), ("pow2", 1)]
+
+
+def _data(seed, shape, sigma=1.0, frac=0.01, factor=100.0):
+    rng = np.random.default_rng(seed)
+    return add_outliers(rng, normal_f32(rng, shape, sigma), frac, factor)
+
+
+def _to_dev(x_f32, dtype):
+    """Device tensor plus the exact float32 values the oracle must see."""
+    if dtype == "bf16":
+        bits = to_bf16_bits(x_f32)
+        return dev_bf16(bits), oq.bf16_bits_to_f32(bits)
+    return dev(x_f32), x_f32
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode_name,mode", MODES)
+@pytest.mark.parametrize("shape", [(128, 256), (37, 384), (1, 128), (300, 1024)])
+def test_quant_1x128(dtype, mode_name, mode, shape):
+    fp8q = require_gpu()
+    x_dev, x_ref = _to_dev(_data(hash(shape) % 1000, shape), dtype)
+    q, s = fp8q.fp8_quant_tile(x_dev, fp8q.TILE_1x128, mode)
+    q_ref, s_ref = oq.quant_1x128(x_ref, mode_name)
+    assert_bytes_equal(host(q), q_ref, "codes")
+    assert_bytes_equal(host(s), s_ref, "scales")
+
+
+def _edge_tensor_f32():
+    """Rows whose first element is 448*2^k (so inv = 2^-k exactly) followed by
+    127 values that sweep the converter's rounding cases."""
+    mags = e4m3.decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (0.5 * (mags[:-1] + mags[1:])).astype(np.float32)
+    pts = np.concatenate([mags.astype(np.float32), mids])
+    bits = pts.view(np.int32).astype(np.int64)[:, None] + np.arange(-3, 4)[None, :]
+    sweep = bits.reshape(-1)
+    sweep = sweep[sweep >= 0].astype(np.int32).view(np.float32)
+    sweep = sweep[np.abs(sweep) <= 448.0]
+    sweep = np.concatenate([sweep, -sweep, np.array([0.0, -0.0, 1e-45, -1e-45, 1e-39, -1e-39], np.float32)])
+    n_rows = -(-sweep.size // 127)
+    sweep = np.concatenate([sweep, np.zeros(n_rows * 127 - sweep.size, np.float32)])
+    body = sweep.reshape(n_rows, 127)
+    rows = []
+    for k in (0, -3, 5):
+        head = np.full((n_rows, 1), np.float32(448.0 * 2.0 ** k))
+        rows.append(np.concatenate([head, body * np.float32(2.0 ** k)], axis=1))
+    special = np.zeros((6, 128), np.float32)
+    special[1, :] = -0.0                             # all negative zeros
+    special[2, 3] = np.float32(1e-40)                # subnormal max-abs
+    special[3, :] = np.float32(-0.02)                # constant tile
+    special[4, 0] = np.float32(3e38)                 # near FP32 max
+    special[4, 1:] = np.float32(1e30)
+    special[5, 0] = np.float32(3.6)                  # pow2 rounds the exponent up
+    return np.concatenate(rows + [special], axis=0).astype(np.float32)
+
+
+@pytest.mark.parametrize("mode_name,mode", MODES)
+def test_quant_1x128_edge_values_f32(mode_name, mode):
+    fp8q = require_gpu()
+    x = _edge_tensor_f32()
+    q, s = fp8q.fp8_quant_tile(dev(x), fp8q.TILE_1x128, mode)
+    q_ref, s_ref = oq.quant_1x128(x, mode_name)
+    assert_bytes_equal(host(s), s_ref, "scales")
+    assert_bytes_equal(host(q), q_ref, "codes")
+
+
+@pytest.mark.parametrize("mode_name,mode", MODES)
+def test_quant_1x128_every_bf16_pattern(mode_name, mode):
+    """All 65536 BF16 patterns that are finite, arranged 127 per tile behind a
+    448 (max-abs 448 -> unit scale) and behind 448*2^-20."""
+    fp8q = require_gpu()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oq.bf16_bits_to_f32(bits)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    bits = bits[keep]
+    n_rows = -(-bits.size // 127)
+    bits = np.concatenate([bits, np.zeros(n_rows * 127 - bits.size, np.uint16)]).reshape(n_rows, 127)
+    head = np.full((n_rows, 1), 0x43E0, np.uint16)                 # 448.0 in BF16
+    x_bits = np.concatenate([head, bits], axis=1)
+    # second copy scaled by 2^-20 (exact in BF16 for normal values; tiny ones flush as BF16 would not)
+    small = oq.bf16_bits_to_f32(x_bits) * np.float32(2.0 ** -20)
+    x_bits = np.concatenate([x_bits, to_bf16_bits(small)], axis=0)
+    q, s = fp8q.fp8_quant_tile(dev_bf16(x_bits), fp8q.TILE_1x128, mode)
+    q_ref, s_ref = oq.quant_1x128(oq.bf16_bits_to_f32(x_bits), mode_name)
+    assert_bytes_equal(host(s), s_ref, "scales")
+    assert_bytes_equal(host(q), q_ref, "codes")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode_name,mode", MODES)
+@pytest.mark.parametrize("shape", [(128, 8), (256, 200), (384, 64), (128, 1000)])
+def test_quant_128x1(dtype, mode_name, mode, shape):
+    fp8q = require_gpu()
+    x_dev, x_ref = _to_dev(_data(7 + shape[1], shape), dtype)
+    qt, s = fp8q.fp8_quant_tile(x_dev, fp8q.TILE_128x1, mode)
+    qt_ref, s_ref = oq.quant_128x1(x_ref, mode_name)
+    assert_bytes_equal(host(qt), qt_ref, "transposed codes")
+    assert_bytes_equal(host(s), s_ref, "scales")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode_name,mode", MODES)
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 256)])
+def test_quant_block(dtype, mode_name, mode, shape):
+    fp8q = require_gpu()
+    x_dev, x_ref = _to_dev(_data(11 + shape[0], shape, sigma=0.02), dtype)
+    q, s, qt, st = fp8q.fp8_quant_block(x_dev, mode, transposed=True)
+    q_ref, s_ref = oq.quant_128x128(x_ref, mode_name)
+    assert_bytes_equal(host(q), q_ref, "codes")
+    assert_bytes_equal(host(s), s_ref, "scales")
+    assert_bytes_equal(host(qt), np.ascontiguousarray(q_ref.T), "transposed codes")
+    assert_bytes_equal(host(st), np.ascontiguousarray(s_ref.T), "transposed scales")
+    q2, s2 = fp8q.fp8_quant_block(x_dev, mode, transposed=False)
+    assert_bytes_equal(host(q2), q_ref, "codes without the transposed copy")
+
+
+def test_quant_strided_input_and_outputs():
+    """Leading dimensions larger than the logical width (a column slice)."""
+    fp8q = require_gpu()
+    full = _data(5, (256, 512))
+    bits = to_bf16_bits(full)
+    x_dev = dev_bf16(bits)[:, 128:384]                       # ld 512, width 256
+    q_store = torch.zeros((256, 320), dtype=torch.uint8, device="cuda")
+    q, s = fp8q.fp8_quant_tile(x_dev, fp8q.TILE_1x128, 0, q=q_store[:, :256])
+    q_ref, s_ref = oq.quant_1x128(oq.bf16_bits_to_f32(bits[:, 128:384]), "maxabs")
+    assert_bytes_equal(host(q_store)[:, :256], q_ref, "codes")
+    assert np.all(host(q_store)[:, 256:] == 0)
+    assert_bytes_equal(host(s), s_ref, "scales")
+
+
+def test_quantizers_deterministic():
+    fp8q = require_gpu()
+    x_dev, _ = _to_dev(_data(3, (512, 1024)), "bf16")
+    a = [host(t) for t in fp8q.fp8_quant_tile(x_dev, fp8q.TILE_1x128, 0)]
+    b = [host(t) for t in fp8q.fp8_quant_tile(x_dev, fp8q.TILE_1x128, 0)]
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads, checked on sampled rows / columns / bands.
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def layer():
+    d = linear_layer()
+    return d, dev_bf16(d["x"]), dev_bf16(d["wt"])
+
+
+@pytest.mark.parametrize("mode_name,mode", MODES)
+def test_full_activation_1x128_sampled_rows(layer, mode_name, mode):
+    fp8q = require_gpu()
+    d, x_dev, _ = layer
+    q, s = fp8q.fp8_quant_tile(x_dev, fp8q.TILE_1x128, mode)
+    rows = np.sort(np.random.default_rng(21).choice(8192, 48, replace=False))
+    rows = np.concatenate([rows, [0, 8191]])
+    q_ref, s_ref = oq.quant_1x128(oq.bf16_bits_to_f32(d["x"][rows]), mode_name)
+    assert_bytes_equal(host(q[torch.as_tensor(rows).cuda()]), q_ref, "codes")
+    assert_bytes_equal(host(s)[:, rows], s_ref, "scales")
+
+
+def test_full_weight_block_sampled_bands(layer):
+    fp8q = require_gpu()
+    d, _, w_dev = layer
+    q, s, qt, st = fp8q.fp8_quant_block(w_dev, 0, transposed=True)
+    qh, sh, qth, sth = host(q), host(s), host(qt), host(st)
+    for band in (0, 77, 143):                                   # 128-row bands of the [18432][7168] weight
+        rs = slice(band * 128, (band + 1) * 128)
+        q_ref, s_ref = oq.quant_128x128(oq.bf16_bits_to_f32(d["wt"][rs]), "maxabs")
+        assert_bytes_equal(qh[rs], q_ref, f"band {band} codes")
+        assert_bytes_equal(sh[band], s_ref[0], f"band {band} scales")
+        assert_bytes_equal(qth[:, rs], np.ascontiguousarray(q_ref.T), f"band {band} transposed codes")
+        assert_bytes_equal(sth[:, band], s_ref[0], f"band {band} transposed scales")
+
+
+def test_full_wgrad_operands_128x1_sampled_columns(layer):
+    fp8q = require_gpu()
+    d, x_dev, _ = layer
+    qt, s = fp8q.fp8_quant_tile(x_dev, fp8q.TILE_128x1, 0)
+    cols = np.sort(np.random.default_rng(22).choice(7168, 40, replace=False))
+    qt_ref, s_ref = oq.quant_128x1(oq.bf16_bits_to_f32(d["x"][:, cols]), "maxabs")
+    assert_bytes_equal(host(qt)[cols], qt_ref, "transposed codes")
+    assert_bytes_equal(host(s)[:, cols], s_ref, "scales")
+
+
+def test_full_output_grad_both_tilings_sampled():
+    fp8q = require_gpu()
+    dy = output_grad()["dy"]
+    dy_dev = dev_bf16(dy)
+    q, s = fp8q.fp8_quant_tile(dy_dev, fp8q.TILE_1x128, 0)
+    rows = np.sort(np.random.default_rng(23).choice(8192, 24, replace=False))
+    q_ref, s_ref = oq.quant_1x128(oq.bf16_bits_to_f32(dy[rows]), "maxabs")
+    assert_bytes_equal(host(q)[rows], q_ref, "1x128 codes")
+    assert_bytes_equal(host(s)[:, rows], s_ref, "1x128 scales")
+    del q, s
+    qt, s = fp8q.fp8_quant_tile(dy_dev, fp8q.TILE_128x1, 1)
+    cols = np.sort(np.random.default_rng(24).choice(18432, 24, replace=False))
+    qt_ref, s_ref = oq.quant_128x1(oq.bf16_bits_to_f32(dy[:, cols]), "pow2")
+    assert_bytes_equal(host(qt)[cols], qt_ref, "128x1 codes")
+    assert_bytes_equal(host(s)[:, cols], s_ref, "128x1 scales")
