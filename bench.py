@@ -1,0 +1,287 @@
+"""Benchmark of the fine-grained FP8 training hot path on one MI355X.
+
+One step = every stage of the path over one batch of synthetic input:
+  * FP8 Linear layer, 8192 tokens, 7168 -> 18432 channels, forward + backward:
+      1x128 quantization of X (bf16) and of dY (bf16),
+      128x128 quantization of the weight (bf16, stored [out][in]) with its
+        transposed copy for Dgrad,
+      128x1 quantization of dY and X for Wgrad,
+      Fprop  Y  = X W       (M=8192,  N=18432, K=7168,  BF16 out),
+      Dgrad  dX = dY W^T    (M=8192,  N=7168,  K=18432, BF16 out),
+      Wgrad  dW = dY^T X    (M=18432, N=7168,  K=8192,  FP32 out);
+  * MoE expert layer forward: 64 experts, 65536 routed tokens (Zipf 1.1,
+    rows padded to 128), K=7168, N=2048: 1x128 quantization of the tokens,
+    128x128 quantization of the stacked expert weights, grouped Fprop (BF16 out).
+
+value = useful GEMM FLOP of the step (padding rows excluded) / step time, in
+TFLOP/s; every kernel of the step is inside the timed region.  Per-kernel
+durations come from HIP events recorded on the stream the kernels run on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--copy-calibration]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s & % FP8 MFMA peak; quantizer GB/s (1 GPU)"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+T, D_IN, D_OUT = 8192, 7168, 18432
+G_MOE, N_MOE = 64, 2048
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    return p.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("quant.hip", "gemm.hip", "fp8q_device.h"):
+        with open(os.path.join(ROOT, "precision_fp8_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Step:
+    """Device buffers and the kernel sequence of one step."""
+
+    def __init__(self, fp8q):
+        from tests.helpers import dev_bf16   # plain host->device copy helper
+        from workloads import linear_layer, moe_layer, output_grad
+        self.fp8q = fp8q
+        t0 = time.time()
+        lin = linear_layer()
+        dy = output_grad()["dy"]
+        moe = moe_layer()
+        log(f"[bench] synthetic inputs generated in {time.time() - t0:.1f}s")
+        self.x, self.wt, self.dy = dev_bf16(lin["x"]), dev_bf16(lin["wt"]), dev_bf16(dy)
+        self.mx, self.mw = dev_bf16(moe["x"]), dev_bf16(moe["wt"])
+        self.gmap = torch.from_numpy(moe["group_of_mtile"]).cuda()
+        self.moe_tokens = int(moe["counts"].sum())
+        self.m_pad = moe["x"].shape[0]
+        del lin, dy, moe
+        dev = self.x.device
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        # quantized operands
+        self.qx, self.sx = e((T, D_IN), u8), e((D_IN // 128, T), f32)
+        self.qw, self.sw = e((D_OUT, D_IN), u8), e((D_OUT // 128, D_IN // 128), f32)
+        self.qwt, self.swt = e((D_IN, D_OUT), u8), e((D_IN // 128, D_OUT // 128), f32)
+        self.qdy, self.sdy = e((T, D_OUT), u8), e((D_OUT // 128, T), f32)
+        self.qdyt, self.sdyt = e((D_OUT, T), u8), e((T // 128, D_OUT), f32)
+        self.qxt, self.sxt = e((D_IN, T), u8), e((T // 128, D_IN), f32)
+        self.qmx, self.smx = e((self.m_pad, D_IN), u8), e((D_IN // 128, self.m_pad), f32)
+        self.qmw, self.smw = e((G_MOE * N_MOE, D_IN), u8), e((G_MOE * N_MOE // 128, D_IN // 128), f32)
+        # outputs
+        self.y, self.dx = e((T, D_OUT), bf), e((T, D_IN), bf)
+        self.dw = e((D_OUT, D_IN), f32)
+        self.my = e((self.m_pad, N_MOE), bf)
+        self.pow2_q, self.pow2_s = e((T, D_IN), u8), e((D_IN // 128, T), f32)
+
+        bf16_quant_bytes = lambda r, c: r * c * 2 + r * c + (r * c // 128) * 4      # in + codes + scales
+        block_bytes = lambda r, c, t: r * c * 2 + r * c * (2 if t else 1) + (r // 128) * (c // 128) * 4 * (2 if t else 1)
+        gf = lambda m, n, k: 2.0 * m * n * k
+        # (name, launch fn, algorithmic work, kind of work)
+        q = fp8q
+        self.kernels = [
+            ("quant_1x128 X", lambda: q.fp8_quant_tile(self.x, q.TILE_1x128, q.MAXABS, self.qx, self.sx),
+             bf16_quant_bytes(T, D_IN), "bytes"),
+            ("quant_128x128 W (+transposed)", lambda: q.fp8_quant_block(self.wt, q.MAXABS, True, self.qw, self.sw,
+                                                                       self.qwt, self.swt),
+             block_bytes(D_OUT, D_IN, True), "bytes"),
+            ("gemm Fprop", lambda: q.fp8_gemm_blockscaled(q.FPROP, self.qx, self.sx, self.qw, self.sw, c=self.y),
+             gf(T, D_OUT, D_IN), "flop"),
+            ("quant_1x128 dY", lambda: q.fp8_quant_tile(self.dy, q.TILE_1x128, q.MAXABS, self.qdy, self.sdy),
+             bf16_quant_bytes(T, D_OUT), "bytes"),
+            ("gemm Dgrad", lambda: q.fp8_gemm_blockscaled(q.DGRAD, self.qdy, self.sdy, self.qwt, self.swt, c=self.dx),
+             gf(T, D_IN, D_OUT), "flop"),
+            ("quant_128x1 dY", lambda: q.fp8_quant_tile(self.dy, q.TILE_128x1, q.MAXABS, self.qdyt, self.sdyt),
+             bf16_quant_bytes(T, D_OUT), "bytes"),
+            ("quant_128x1 X", lambda: q.fp8_quant_tile(self.x, q.TILE_128x1, q.MAXABS, self.qxt, self.sxt),
+             bf16_quant_bytes(T, D_IN), "bytes"),
+            ("gemm Wgrad", lambda: q.fp8_gemm_blockscaled(q.WGRAD, self.qdyt, self.sdyt, self.qxt, self.sxt, c=self.dw),
+             gf(D_OUT, D_IN, T), "flop"),
+            ("quant_1x128 MoE tokens", lambda: q.fp8_quant_tile(self.mx, q.TILE_1x128, q.MAXABS, self.qmx, self.smx),
+             bf16_quant_bytes(self.m_pad, D_IN), "bytes"),
+            ("quant_128x128 MoE weights", lambda: q.fp8_quant_block(self.mw, q.MAXABS, False, self.qmw, self.smw),
+             block_bytes(G_MOE * N_MOE, D_IN, False), "bytes"),
+            ("gemm grouped MoE", lambda: q.fp8_gemm_blockscaled_grouped(
+                self.gmap, self.qmx, self.smx, self.qmw.view(G_MOE, N_MOE, D_IN),
+                self.smw.view(G_MOE, N_MOE // 128, D_IN // 128), c=self.my),
+             gf(self.moe_tokens, N_MOE, D_IN), "flop"),
+        ]
+        self.extra = [
+            ("quant_1x128 X (pow2 scales)", lambda: q.fp8_quant_tile(self.x, q.TILE_1x128, q.POW2,
+                                                                     self.pow2_q, self.pow2_s),
+             bf16_quant_bytes(T, D_IN), "bytes"),
+        ]
+        self.step_flop = sum(w for _, _, w, kind in self.kernels if kind == "flop")
+
+    def run(self, events=None):
+        for i, (_, fn, _, _) in enumerate(self.kernels):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on a bounded slice of the Fprop stage."""
+    from threadpoolctl import threadpool_info
+    from oracle import gemm as og, quant as oq
+    from workloads import bf16_bits_as_f32, linear_layer
+    m, n = 1024, 8192
+    d = linear_layer()
+    x = bf16_bits_as_f32(d["x"][:m])
+    wt = bf16_bits_as_f32(d["wt"][:n])
+    del d
+    t0 = time.perf_counter()
+    qa, sa = oq.quant_1x128(x)
+    qb, sb = oq.quant_128x128(wt)
+    og.gemm_ref(qa, sa, qb, sb, og.FPROP)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * m * n * D_IN
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": max(blas + [1]), "kind": "oracle",
+            "sample": f"Fprop slice M={m} tokens, N={n}, K={D_IN}: oracle 1x128 + 128x128 quantization of "
+                      f"the slices and the exact per-K-group GEMM, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported in this build "
+              "(the path's multi-GPU sharding is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+    import precision_fp8_quant_amd as fp8q
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    torch.cuda.set_device(0)
+    step = Step(fp8q)
+
+    # untimed warm-up
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    nk = len(step.kernels)
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step.run(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
+
+    per_kernel = {}
+    for i, (name, _, work, kind) in enumerate(step.kernels):
+        us = float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)])) * 1e3
+        per_kernel[name] = _kernel_entry(us, work, kind)
+
+    # extra kernels outside the step (pow2 scale mode of the activation quantizer)
+    for name, fn, work, kind in step.extra:
+        for _ in range(2):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        per_kernel[name] = dict(_kernel_entry(us, work, kind), outside_step=True)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        per_kernel["calibration copy 1 GiB"] = dict(_kernel_entry(a.elapsed_time(b) * 1e3, 2 << 30, "bytes"),
+                                                    outside_step=True)
+
+    ms_per_step = elapsed / args.steps * 1e3
+    value = step.step_flop / (elapsed / args.steps) / 1e12
+
+    in_step = {k: v for k, v in per_kernel.items() if not v.get("outside_step")}
+    dom_name = max(in_step, key=lambda k: in_step[k]["us"])
+    dom = in_step[dom_name]
+    roof = _roofline(dom_name, dom)
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f8e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "FP8 Linear fwd+bwd (8192 tokens, 7168->18432) + MoE grouped Fprop "
+                               "(64 experts, 65536 tokens Zipf(1.1), 7168->2048)",
+                   "tokens": T, "d_in": D_IN, "d_out": D_OUT, "moe_experts": G_MOE, "moe_tokens": step.moe_tokens,
+                   "moe_rows_padded": step.m_pad, "scale_mode": "maxabs", "parallelism": "single GPU"},
+        "gemm_flop_per_step": step.step_flop,
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_entry(us, work, kind):
+    if kind == "flop":
+        tf = work / (us * 1e-6) / 1e12
+        return {"us": round(us, 2), "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                "flop": work}
+    gbs = work / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "gbs": round(gbs, 1), "frac_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": work}
+
+
+def _roofline(name, k):
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as fh:
+            t = json.load(fh)
+        if t.get("source_hash") == source_hash() and name in t.get("kernels", {}):
+            traffic = t["kernels"][name]
+    if "tflops" in k:
+        return {"kernel": name, "bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(k["tflops"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "avg_us": k["us"]}
+    return {"kernel": name, "bound": "hbm", "achieved": k["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(k["gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic, "avg_us": k["us"]}
+
+
+if __name__ == "__main__":
+    main()
