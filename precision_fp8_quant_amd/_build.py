@@ -25,8 +25,10 @@ HOST_SOURCES = ["abi.cpp"]
 # back); the GEMM asks for its FMAs explicitly.
 # -packed-fp32-ops off: keep the compiler from forming packed FP32 VALU ops.
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-I", INCLUDE, "-I", CSRC]
+# -amdgpu-mfma-vgpr-form: MFMA results go straight to VGPRs, where the FP32
+# promotion FMAs read them (no v_accvgpr_read copies).
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-Wno-unused-command-line-argument"]
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-unused-command-line-argument"]
 
 
 def _run(cmd, verbose):

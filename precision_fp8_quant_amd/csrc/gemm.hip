@@ -53,26 +53,56 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return u >> 16;
 }
 
-// LDS address (bytes) of 16-byte chunk `chunk` (0..7) of tile row `row`.
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+// Swizzle of the eight 16-byte chunks of a 128-byte LDS tile row.  A
+// fragment read touches 16 consecutive rows at one logical chunk; XOR-ing the
+// chunk with (row >> 1) & 7 spreads those 16 reads over 16 distinct 16-byte
+// bank groups (the row's parity picks the 128-byte half of a 256-byte bank line).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
+
+// B tiles are stored in LDS in fragment order: LDS row rho = 64*p + 16*js + r
+// holds global row 64*p + 16*(r/4) + 4*js + r%4, so the 16 rows a fragment
+// needs are consecutive in LDS while a lane still ends up owning 16
+// consecutive output columns.
+__device__ __forceinline__ int b_row_of_lds_row(int rho) {
+  return (rho & ~63) | (((rho & 15) >> 2) << 4) | (((rho >> 4) & 3) << 2) | (rho & 3);
+}
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// 16 bytes per lane from global memory straight into LDS at dst + 16*lane
+// (dst is wave-uniform).  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lq) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + lds_off(row, 2 * lq));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + lds_off(row, 2 * lq + 1));
+  return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
 }
 
 template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs p) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM;          // wave tile rows (M)
   constexpr int TN = BN / WN;          // wave tile cols (N)
   constexpr int SM = TM / 16;          // M subtiles per wave
   constexpr int PN = TN / 64;          // 64-column panels per wave
   static_assert(TM % 16 == 0 && TN % 64 == 0, "wave tile shape");
   static_assert(BSCALE == kScaleRow || 128 % TN == 0, "block-scaled B needs a wave inside one 128-column block");
-  constexpr int A_CHUNKS = BM * 8 / NT;  // 16-byte chunks per thread per group
-  constexpr int B_CHUNKS = BN * 8 / NT;
-  static_assert(A_CHUNKS * NT == BM * 8 && B_CHUNKS * NT == BN * 8, "load split");
-  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int A_BYTES = BM * 128;
+  constexpr int B_BYTES = BN * 128;
+  constexpr int SB_BYTES = BSCALE == kScaleRow ? BN * 4 : 0;
+  constexpr int STAGE = A_BYTES + B_BYTES + SB_BYTES;
+  constexpr int A_DMA = A_BYTES / 1024 / NW;     // 1 KB wave-wide DMA instructions per wave per stage
+  constexpr int B_DMA = B_BYTES / 1024 / NW;
+  static_assert(A_DMA * 1024 * NW == A_BYTES && B_DMA * 1024 * NW == B_BYTES, "DMA split");
+  static_assert(BN <= 256, "row scales: one DMA of at most 64 lanes x 4 floats");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,7 +115,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   const int64_t tiles_n = p.N / BN;
   const int64_t ntiles = tiles_m * tiles_n;
   int64_t bid = blockIdx.x;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);   // consecutive tiles share an XCD
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);   // neighbouring tiles share an XCD
   constexpr int64_t GROUP_M = 8;
   const int64_t per_group = GROUP_M * tiles_n;
   const int64_t first_m = (bid / per_group) * GROUP_M;
@@ -103,40 +133,47 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     bptr += int64_t(grp) * p.b_group_stride;
     sbptr += int64_t(grp) * p.sb_group_stride;
   }
-
   const int64_t KG = p.K >> 7;
 
-  // ---- global -> register staging (thread t moves chunks t, t+NT, ...) ----
-  u32x4 ra[A_CHUNKS], rb[B_CHUNKS];
-#define FP8Q_LOAD_GLOBAL(g)                                                                       \
-  do {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) {                                        \
-      const int idx = tid + i * NT;                                                               \
-      ra[i] = *reinterpret_cast<const u32x4*>(p.a + (m0 + (idx >> 3)) * p.lda + (g) * 128 +        \
-                                              (idx & 7) * 16);                                    \
-    }                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) {                                        \
-      const int idx = tid + i * NT;                                                               \
-      rb[i] = *reinterpret_cast<const u32x4*>(bptr + (n0 + (idx >> 3)) * p.ldb + (g) * 128 +       \
-                                              (idx & 7) * 16);                                    \
-    }                                                                                             \
-  } while (0)
-#define FP8Q_STORE_LDS(stage)                                                                     \
-  do {                                                                                            \
-    uint8_t* base_ = smem + (stage) * STAGE;                                                      \
-    _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) {                                        \
-      const int idx = tid + i * NT;                                                               \
-      *reinterpret_cast<u32x4*>(base_ + lds_off(idx >> 3, idx & 7)) = ra[i];                      \
-    }                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) {                                        \
-      const int idx = tid + i * NT;                                                               \
-      *reinterpret_cast<u32x4*>(base_ + BM * 128 + lds_off(idx >> 3, idx & 7)) = rb[i];           \
-    }                                                                                             \
-  } while (0)
+  // ---- DMA addressing ------------------------------------------------------
+  // Wave-wide DMA instruction `blk` fills LDS rows 8*blk .. 8*blk+7; lane l
+  // lands at row 8*blk + l/8, physical chunk l%8, i.e. logical chunk
+  // (l%8) ^ swz(row).  swz(row) = (4*(blk&1) + l/16) & 7, so the per-lane
+  // byte offsets take one of two values (even / odd blk) and everything else
+  // is wave-uniform (kept in SGPRs).  For B the LDS row rho maps to global
+  // row 64*(blk/8) + 32*(blk&1) + 4*((blk/2)&3)  [uniform]
+  //          + 16*(l/32) + (l/8)%4               [per lane].
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int sw_even = (lane >> 4) & 7, sw_odd = (4 + (lane >> 4)) & 7;
+  const uint32_t a_off[2] = {uint32_t((lane >> 3) * p.lda + (((lane & 7) ^ sw_even) << 4)),
+                             uint32_t((lane >> 3) * p.lda + (((lane & 7) ^ sw_odd) << 4))};
+  const int b_lane_row = 16 * (lane >> 5) + ((lane >> 3) & 3);
+  const uint32_t b_off[2] = {uint32_t(b_lane_row * p.ldb + (((lane & 7) ^ sw_even) << 4)),
+                             uint32_t(b_lane_row * p.ldb + (((lane & 7) ^ sw_odd) << 4))};
+  const uint8_t* a_base = p.a + m0 * p.lda;
+  const uint8_t* b_base = bptr + n0 * p.ldb;
+
+  auto issue_stage = [&](int64_t g, int stage) {
+    uint8_t* base = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+      const int blk = wave_u * A_DMA + i;
+      dma16(a_base + int64_t(8 * blk) * p.lda + g * 128 + a_off[blk & 1], base + blk * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+      const int blk = wave_u * B_DMA + i;
+      const int row_u = 64 * (blk >> 3) + 32 * (blk & 1) + 4 * ((blk >> 1) & 3);
+      dma16(b_base + int64_t(row_u) * p.ldb + g * 128 + b_off[blk & 1], base + A_BYTES + blk * 1024);
+    }
+    if constexpr (BSCALE == kScaleRow) {
+      if (wave_u == NW - 1 && lane < BN / 4) dma16(sbptr + g * p.N + n0 + lane * 4, base + A_BYTES + B_BYTES);
+    }
+  };
 
   // ---- per-lane output coordinates ----------------------------------------
-  const int lr = lane & 15;          // m within a subtile / source row of a fragment
-  const int lq = lane >> 4;          // K quarter of a fragment; 16-column run of a panel
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
   const int64_t m_lane = m0 + wm * TM + lr;                 // + 16*ms
   const int64_t n_wave = n0 + wn * TN;                      // + 64*pn + 16*lq + 4*js + j
 
@@ -150,76 +187,69 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
 #pragma unroll
         for (int d = 0; d < 4; ++d) acc[a][b][c][d] = 0.0f;
 
+  // scales of the current group, prefetched one group ahead
+  float sa_cur[SM], sa_nxt[SM];
+  float sb_cur = 0.0f, sb_nxt = 0.0f;
   if (KG > 0) {
-    FP8Q_LOAD_GLOBAL(0);
-    FP8Q_STORE_LDS(0);
+    issue_stage(0, 0);
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) sa_cur[ms] = p.sa[m_lane + 16 * ms];
+    if constexpr (BSCALE == kScaleBlock) sb_cur = sbptr[(n_wave >> 7) * KG];
+    wait_vmem_all();
   }
   __syncthreads();
 
+  // One basic block per iteration (no branches between the MFMAs and their
+  // promotion FMAs): the last iteration simply re-fetches its own group into
+  // the idle stage, which nobody reads.
   for (int64_t g = 0; g < KG; ++g) {
     const int stage = int(g & 1);
-    if (g + 1 < KG) FP8Q_LOAD_GLOBAL(g + 1);
+    const int64_t gn = g + 1 < KG ? g + 1 : g;
+    issue_stage(gn, stage ^ 1);
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) sa_nxt[ms] = p.sa[gn * p.M + m_lane + 16 * ms];
+    if constexpr (BSCALE == kScaleBlock) sb_nxt = sbptr[(n_wave >> 7) * KG + gn];
 
-    // scales for this group
-    float sa_v[SM];
+    const uint8_t* ta = smem + stage * STAGE;
+    const uint8_t* tb = ta + A_BYTES;
+    float cs[SM];
 #pragma unroll
-    for (int ms = 0; ms < SM; ++ms) sa_v[ms] = p.sa[g * p.M + m_lane + 16 * ms];
-    float sb_blk = 0.0f;
-    float sb_col[PN][4][4];
-    if constexpr (BSCALE == kScaleBlock) {
-      sb_blk = sbptr[(n_wave >> 7) * KG + g];
+    for (int ms = 0; ms < SM; ++ms) cs[ms] = BSCALE == kScaleBlock ? sa_cur[ms] * sb_cur : sa_cur[ms];
+
+    // A fragments for the whole group; B fragments one ahead of their use.
+    // The scheduling barrier at the end of each B fragment keeps the compiler
+    // from hoisting every B fragment read (which would not fit in 256 VGPRs
+    // with two waves per SIMD).
+    v8i af[SM];
 #pragma unroll
-      for (int ms = 0; ms < SM; ++ms) sa_v[ms] *= sb_blk;
-    } else {
+    for (int ms = 0; ms < SM; ++ms) af[ms] = read_frag(ta, wm * TM + 16 * ms + lr, lq);
+    v8i bfb[2];
+    bfb[0] = read_frag(tb, wn * TN + lr, lq);
 #pragma unroll
-      for (int pn = 0; pn < PN; ++pn) {
-        const v4f* src = reinterpret_cast<const v4f*>(sbptr + g * p.N + n_wave + 64 * pn + 16 * lq);
+    for (int t = 0; t < PN * 4; ++t) {
+      const int pn = t >> 2, js = t & 3;
+      if (t + 1 < PN * 4) bfb[(t + 1) & 1] = read_frag(tb, wn * TN + 16 * (t + 1) + lr, lq);
+      const v8i bf = bfb[t & 1];
+      v4f sbv = {1.0f, 1.0f, 1.0f, 1.0f};
+      if constexpr (BSCALE == kScaleRow)
+        sbv = *reinterpret_cast<const v4f*>(tb + B_BYTES + (wn * TN + 64 * pn + 16 * lq + 4 * js) * 4);
 #pragma unroll
-        for (int js = 0; js < 4; ++js) {
-          const v4f s4 = src[js];
-          sb_col[pn][js][0] = s4.x; sb_col[pn][js][1] = s4.y;
-          sb_col[pn][js][2] = s4.z; sb_col[pn][js][3] = s4.w;
+      for (int ms = 0; ms < SM; ++ms) {
+        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[ms], zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float dj = BSCALE == kScaleRow ? d[j] * sbv[j] : d[j];
+          acc[ms][pn][js][j] = __builtin_fmaf(dj, cs[ms], acc[ms][pn][js][j]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // fragments
-    const uint8_t* sbase = smem + stage * STAGE;
-    v8i afrag[SM];
 #pragma unroll
-    for (int ms = 0; ms < SM; ++ms) {
-      const int row = wm * TM + 16 * ms + lr;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(sbase + lds_off(row, 2 * lq));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(sbase + lds_off(row, 2 * lq + 1));
-      afrag[ms] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-    }
-#pragma unroll
-    for (int pn = 0; pn < PN; ++pn) {
-#pragma unroll
-      for (int js = 0; js < 4; ++js) {
-        const int row = wn * TN + 64 * pn + 16 * (lr >> 2) + 4 * js + (lr & 3);
-        const uint8_t* bb = sbase + BM * 128;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(bb + lds_off(row, 2 * lq));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(bb + lds_off(row, 2 * lq + 1));
-        const v8i bfrag = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-#pragma unroll
-        for (int ms = 0; ms < SM; ++ms) {
-          const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfrag, afrag[ms], zero,
-                                                                        0, 0, 0, 0, 0, 0);
-          if constexpr (BSCALE == kScaleBlock) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[ms][pn][js][j] = __builtin_fmaf(d[j], sa_v[ms], acc[ms][pn][js][j]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[ms][pn][js][j] = __builtin_fmaf(d[j] * sb_col[pn][js][j], sa_v[ms], acc[ms][pn][js][j]);
-          }
-        }
-      }
-    }
-
-    if (g + 1 < KG) FP8Q_STORE_LDS(stage ^ 1);
+    for (int ms = 0; ms < SM; ++ms) sa_cur[ms] = sa_nxt[ms];
+    sb_cur = sb_nxt;
+    wait_vmem_all();
     __syncthreads();
   }
 
@@ -253,9 +283,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   }
 }
 
-#undef FP8Q_LOAD_GLOBAL
-#undef FP8Q_STORE_LDS
-
 // ---------------------------------------------------------------------------
 // Launch configurations.
 // ---------------------------------------------------------------------------
@@ -268,13 +295,25 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Tile configurations, largest that divides the problem:
+//   256x256, 8 waves (4 along M x 2 along N) of 64x128
+//   128x256, 4 waves (2x2) of 64x128  (also every grouped GEMM: one group per 128-row tile)
+//   256x128, 4 waves (4x1) of 64x128
+//   128x128, 4 waves (2x2) of 64x64
+template <int BSCALE, int OUT, bool GROUPED>
+static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
+  if (!GROUPED && a.M % 256 == 0 && a.N % 256 == 0) return launch_cfg<256, 256, 4, 2, BSCALE, OUT, GROUPED>(a, st);
+  if (a.N % 256 == 0) return launch_cfg<128, 256, 2, 2, BSCALE, OUT, GROUPED>(a, st);
+  if (!GROUPED && a.M % 256 == 0) return launch_cfg<256, 128, 4, 1, BSCALE, OUT, GROUPED>(a, st);
+  return launch_cfg<128, 128, 2, 2, BSCALE, OUT, GROUPED>(a, st);
+}
+
 template <int BSCALE, bool GROUPED>
 static hipError_t launch_out(const GemmArgs& a, int out, hipStream_t st) {
-  // 128x128 workgroup tile, 2x2 waves of 64x64.
   switch (out) {
-    case kOutBF16: return launch_cfg<128, 128, 2, 2, BSCALE, kOutBF16, GROUPED>(a, st);
-    case kOutF32: return launch_cfg<128, 128, 2, 2, BSCALE, kOutF32, GROUPED>(a, st);
-    default: return launch_cfg<128, 128, 2, 2, BSCALE, kOutF32Acc, GROUPED>(a, st);
+    case kOutBF16: return launch_tiles<BSCALE, kOutBF16, GROUPED>(a, st);
+    case kOutF32: return launch_tiles<BSCALE, kOutF32, GROUPED>(a, st);
+    default: return launch_tiles<BSCALE, kOutF32Acc, GROUPED>(a, st);
   }
 }
 
