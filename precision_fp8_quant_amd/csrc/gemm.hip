@@ -53,11 +53,16 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return u >> 16;
 }
 
-// Swizzle of the eight 16-byte chunks of a 128-byte LDS tile row.  A
-// fragment read touches 16 consecutive rows at one logical chunk; XOR-ing the
-// chunk with (row >> 1) & 7 spreads those 16 reads over 16 distinct 16-byte
-// bank groups (the row's parity picks the 128-byte half of a 256-byte bank line).
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// LDS tile rows are 128 bytes (one K-group) in eight 16-byte chunks; chunk c
+// of row r is stored at position c ^ (r & 7).  The K order inside one MFMA
+// is free as long as both operands use the same one, so lane quarter q
+// (lanes 16q..16q+15) feeds its fragment from chunks q and q+4.  The LDS
+// serves a ds_read_b128 in four passes of 16 lanes -- lanes whose 4-lane
+// group index has even / odd bit parity, per half-wave -- over 64 four-byte
+// banks (256 bytes); with this chunk assignment and swizzle every pass of both
+// fragment reads touches 16 distinct 16-byte bank groups (no conflicts),
+// while the DMA still moves whole 128-byte rows.
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
 // B tiles are stored in LDS in fragment order: LDS row rho = 64*p + 16*js + r
@@ -79,8 +84,8 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lq) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + lds_off(row, 2 * lq));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + lds_off(row, 2 * lq + 1));
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + lds_off(row, lq));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + lds_off(row, lq + 4));
   return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
 }
 
@@ -138,18 +143,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   // ---- DMA addressing ------------------------------------------------------
   // Wave-wide DMA instruction `blk` fills LDS rows 8*blk .. 8*blk+7; lane l
   // lands at row 8*blk + l/8, physical chunk l%8, i.e. logical chunk
-  // (l%8) ^ swz(row).  swz(row) = (4*(blk&1) + l/16) & 7, so the per-lane
-  // byte offsets take one of two values (even / odd blk) and everything else
-  // is wave-uniform (kept in SGPRs).  For B the LDS row rho maps to global
-  // row 64*(blk/8) + 32*(blk&1) + 4*((blk/2)&3)  [uniform]
-  //          + 16*(l/32) + (l/8)%4               [per lane].
+  // (l%8) ^ swz(row) = (l%8) ^ (l/8).  The per-lane byte offset is the same
+  // for every blk and everything else is wave-uniform (SGPRs).  For B the LDS
+  // row rho maps to global row 64*(blk/8) + 32*(blk&1) + 4*((blk/2)&3)
+  // [uniform] + 16*(l/32) + (l/8)%4 [per lane].
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int sw_even = (lane >> 4) & 7, sw_odd = (4 + (lane >> 4)) & 7;
-  const uint32_t a_off[2] = {uint32_t((lane >> 3) * p.lda + (((lane & 7) ^ sw_even) << 4)),
-                             uint32_t((lane >> 3) * p.lda + (((lane & 7) ^ sw_odd) << 4))};
-  const int b_lane_row = 16 * (lane >> 5) + ((lane >> 3) & 3);
-  const uint32_t b_off[2] = {uint32_t(b_lane_row * p.ldb + (((lane & 7) ^ sw_even) << 4)),
-                             uint32_t(b_lane_row * p.ldb + (((lane & 7) ^ sw_odd) << 4))};
+  const int lchunk = ((lane & 7) ^ (lane >> 3)) << 4;
+  const uint32_t a_off = uint32_t((lane >> 3) * p.lda + lchunk);
+  const uint32_t b_off = uint32_t((16 * (lane >> 5) + ((lane >> 3) & 3)) * p.ldb + lchunk);
   const uint8_t* a_base = p.a + m0 * p.lda;
   const uint8_t* b_base = bptr + n0 * p.ldb;
 
@@ -158,13 +159,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
       const int blk = wave_u * A_DMA + i;
-      dma16(a_base + int64_t(8 * blk) * p.lda + g * 128 + a_off[blk & 1], base + blk * 1024);
+      dma16(a_base + int64_t(8 * blk) * p.lda + g * 128 + a_off, base + blk * 1024);
     }
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
       const int blk = wave_u * B_DMA + i;
       const int row_u = 64 * (blk >> 3) + 32 * (blk & 1) + 4 * ((blk >> 1) & 3);
-      dma16(b_base + int64_t(row_u) * p.ldb + g * 128 + b_off[blk & 1], base + A_BYTES + blk * 1024);
+      dma16(b_base + int64_t(row_u) * p.ldb + g * 128 + b_off, base + A_BYTES + blk * 1024);
     }
     if constexpr (BSCALE == kScaleRow) {
       if (wave_u == NW - 1 && lane < BN / 4) dma16(sbptr + g * p.N + n0 + lane * 4, base + A_BYTES + B_BYTES);
@@ -216,36 +217,49 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) cs[ms] = BSCALE == kScaleBlock ? sa_cur[ms] * sb_cur : sa_cur[ms];
 
-    // A fragments for the whole group; B fragments one ahead of their use.
-    // The scheduling barrier at the end of each B fragment keeps the compiler
-    // from hoisting every B fragment read (which would not fit in 256 VGPRs
-    // with two waves per SIMD).
+    // Software pipeline over the group's SM*4*PN MFMAs (t = fragment*SM + ms):
+    // MFMA t writes result slot t%3 and the promotion FMAs of MFMA t-2 follow
+    // it, so a VALU op never waits on the MFMA just issued and the matrix pipe
+    // stays fed.  B fragments are read one fragment ahead.  A scheduling
+    // barrier after every step pins this interleave (left alone, the compiler
+    // places each FMA right behind its own MFMA and pads the hazard with s_nop).
+    constexpr int NB = PN * 4;            // B fragments per group
+    constexpr int NT = NB * SM;           // MFMAs per group
+    constexpr int LAG = 2;
     v8i af[SM];
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) af[ms] = read_frag(ta, wm * TM + 16 * ms + lr, lq);
     v8i bfb[2];
     bfb[0] = read_frag(tb, wn * TN + lr, lq);
+    v4f dq[3];
+    v4f sbq[2];
 #pragma unroll
-    for (int t = 0; t < PN * 4; ++t) {
-      const int pn = t >> 2, js = t & 3;
-      if (t + 1 < PN * 4) bfb[(t + 1) & 1] = read_frag(tb, wn * TN + 16 * (t + 1) + lr, lq);
-      const v8i bf = bfb[t & 1];
-      v4f sbv = {1.0f, 1.0f, 1.0f, 1.0f};
-      if constexpr (BSCALE == kScaleRow)
-        sbv = *reinterpret_cast<const v4f*>(tb + B_BYTES + (wn * TN + 64 * pn + 16 * lq + 4 * js) * 4);
-#pragma unroll
-      for (int ms = 0; ms < SM; ++ms) {
-        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[ms], zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float dj = BSCALE == kScaleRow ? d[j] * sbv[j] : d[j];
-          acc[ms][pn][js][j] = __builtin_fmaf(dj, cs[ms], acc[ms][pn][js][j]);
+    for (int t = 0; t < NT + LAG; ++t) {
+      if (t < NT) {
+        const int bi = t / SM, ms = t % SM;
+        if (ms == 0) {
+          if (bi + 1 < NB) bfb[(bi + 1) & 1] = read_frag(tb, wn * TN + 16 * (bi + 1) + lr, lq);
+          if constexpr (BSCALE == kScaleRow)
+            sbq[bi & 1] = *reinterpret_cast<const v4f*>(tb + B_BYTES +
+                                                       (wn * TN + 64 * (bi >> 2) + 16 * lq + 4 * (bi & 3)) * 4);
         }
+        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        dq[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfb[bi & 1], af[ms], zero, 0, 0, 0, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (t >= LAG) {
+        const int u = t - LAG;
+        const int bu = u / SM, mu = u % SM;
+        const int pn = bu >> 2, js = bu & 3;
+        const v4f d = dq[u % 3];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float dj = BSCALE == kScaleRow ? d[j] * sbq[bu & 1][j] : d[j];
+          acc[mu][pn][js][j] = __builtin_fmaf(dj, cs[mu], acc[mu][pn][js][j]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep step t's MFMA and step t-2's FMAs together
     }
-
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) sa_cur[ms] = sa_nxt[ms];
     sb_cur = sb_nxt;
