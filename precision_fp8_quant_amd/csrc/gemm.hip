@@ -226,25 +226,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     constexpr int NB = PN * 4;            // B fragments per group
     constexpr int NT = NB * SM;           // MFMAs per group
     constexpr int LAG = 2;
+    // Fragment reads run ahead of their MFMAs: A fragment ms is read one step
+    // before its first use, B fragment bi two fragments (2*SM steps) ahead.
     v8i af[SM];
-#pragma unroll
-    for (int ms = 0; ms < SM; ++ms) af[ms] = read_frag(ta, wm * TM + 16 * ms + lr, lq);
-    v8i bfb[2];
+    v8i bfb[3];
+    af[0] = read_frag(ta, wm * TM + lr, lq);
     bfb[0] = read_frag(tb, wn * TN + lr, lq);
+    if (NB > 1) bfb[1] = read_frag(tb, wn * TN + 16 + lr, lq);
     v4f dq[3];
     v4f sbq[2];
 #pragma unroll
     for (int t = 0; t < NT + LAG; ++t) {
       if (t < NT) {
         const int bi = t / SM, ms = t % SM;
+        if (bi == 0 && ms + 1 < SM) af[ms + 1] = read_frag(ta, wm * TM + 16 * (ms + 1) + lr, lq);
         if (ms == 0) {
-          if (bi + 1 < NB) bfb[(bi + 1) & 1] = read_frag(tb, wn * TN + 16 * (bi + 1) + lr, lq);
+          if (bi + 2 < NB) bfb[(bi + 2) % 3] = read_frag(tb, wn * TN + 16 * (bi + 2) + lr, lq);
           if constexpr (BSCALE == kScaleRow)
             sbq[bi & 1] = *reinterpret_cast<const v4f*>(tb + B_BYTES +
                                                        (wn * TN + 64 * (bi >> 2) + 16 * lq + 4 * (bi & 3)) * 4);
         }
         const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        dq[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfb[bi & 1], af[ms], zero, 0, 0, 0, 0, 0, 0);
+        dq[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfb[bi % 3], af[ms], zero, 0, 0, 0, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (t >= LAG) {
