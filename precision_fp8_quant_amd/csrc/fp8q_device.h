@@ -3,7 +3,8 @@
 // Quantization arithmetic follows the rule stated in include/fp8q.h:
 // max-abs per group, scale derived from it (max-abs onto E4M3's 448, or the
 // smallest power of two that keeps the group in range), multiply, clamp to
-// +-448, round to E4M3FN with the hardware converter.
+// +-448, round to E4M3FN with the hardware converter (v_cvt_pk_fp8_f32 rounds
+// to nearest-even under the default round mode).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,84 +26,75 @@ struct ScalePair {
   float inv;  // quantization multiplier
 };
 
-// MAXABS: s = a/448 and inv = 448/a, each one IEEE-correct FP32 division
-// (the library is built without fast-math, so '/' is correctly rounded).
-// POW2: s = 2^k with k the least integer such that a <= 448 * 2^k.  Writing
-// a = 1.f * 2^e: 448 = 1.75 * 2^8, so k = e - 8 when 1.f <= 1.75 (mantissa
-// field <= 0x600000) and k = e - 7 otherwise.  a >= 448*2^-126 keeps
-// k >= -126, and a < 2^128 keeps k <= 120, so both 2^k and 2^-k are normal.
-__device__ __forceinline__ ScalePair scale_from_amax(float amax, int mode) {
-  const float a = fmaxf(amax, __uint_as_float(kAmaxFloorBits));
+// fl32(a / 448) for a >= 448 * 2^-126.  448 = 7 * 2^6, so a/448 is fl32(a/7)
+// scaled exactly by 2^-6; fl32(a/7) is the product with fl32(1/7) plus one
+// FMA residual correction.  Checked bit-exact against IEEE division for every
+// float32 in [448 * 2^-126, FLT_MAX] on gfx950.
+__device__ __forceinline__ float div_by_448(float a) {
+  const float c = __uint_as_float(0x3E124925u);          // fl32(1/7)
+  const float q0 = a * c;
+  const float r = __builtin_fmaf(-q0, 7.0f, a);
+  return __builtin_fmaf(r, c, q0) * 0.015625f;
+}
+
+// fl32(448 / a) for a >= 448 * 2^-126: hardware reciprocal, one FMA residual
+// correction.  For a > 2^100 the computation runs on a * 2^-64 (so 1/a stays
+// a normal number) and the result is scaled back exactly.  Checked bit-exact
+// against IEEE division for every float32 in [448 * 2^-126, FLT_MAX] on gfx950.
+__device__ __forceinline__ float div_448_by(float a0) {
+  const bool big = a0 > 0x1p+100f;
+  const float a = big ? a0 * 0x1p-64f : a0;
+  const float y = __builtin_amdgcn_rcpf(a);
+  const float q0 = 448.0f * y;
+  const float r = __builtin_fmaf(-q0, a, 448.0f);
+  return __builtin_fmaf(r, y, q0) * (big ? 0x1p-64f : 1.0f);
+}
+
+// Scale pair from a group's max-abs (given as float32 bits of a non-negative
+// value).  MAXABS: s = fl32(a/448), inv = fl32(448/a).  POW2: s = 2^k with k
+// the least integer such that a <= 448 * 2^k; writing a = 1.f * 2^e with
+// 448 = 1.75 * 2^8, k = e - 8 when 1.f <= 1.75 (mantissa field <= 0x600000)
+// and k = e - 7 otherwise.  a >= 448*2^-126 keeps k >= -126 and a < 2^128
+// keeps k <= 120, so 2^k and 2^-k are normal.
+template <int MODE>
+__device__ __forceinline__ ScalePair scale_from_amax_bits(uint32_t amax_bits) {
+  const uint32_t bits = amax_bits > kAmaxFloorBits ? amax_bits : kAmaxFloorBits;
   ScalePair r;
-  if (mode == kModePow2) {
-    const uint32_t bits = __float_as_uint(a);
-    const int e = int((bits >> 23) & 0xFFu) - 127;
-    const uint32_t frac = bits & 0x7FFFFFu;
-    const int k = (frac <= 0x600000u) ? (e - 8) : (e - 7);
+  if constexpr (MODE == kModePow2) {
+    const int e = int(bits >> 23) - 127;
+    const int k = ((bits & 0x7FFFFFu) <= 0x600000u) ? (e - 8) : (e - 7);
     r.s = __uint_as_float(uint32_t(127 + k) << 23);
     r.inv = __uint_as_float(uint32_t(127 - k) << 23);
   } else {
-    r.s = a / kE4M3Max;
-    r.inv = kE4M3Max / a;
+    const float a = __uint_as_float(bits);
+    r.s = div_by_448(a);
+    r.inv = div_448_by(a);
   }
   return r;
 }
 
-// Max over the 16 lanes of a DPP row (lanes 16r..16r+15), broadcast to all
-// 16.  quad_perm [1,0,3,2] and [2,3,0,1] reduce each quad; row_half_mirror
-// pairs quad i with quad 1-i of the same 8; row_mirror pairs the two halves.
-// Must be called with all 16 lanes of the row active.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+// Unsigned max across the 16 lanes of a DPP row, broadcast to all 16.
+// quad_perm [1,0,3,2] and [2,3,0,1] reduce each quad; row_half_mirror pairs
+// the quads of each half-row; row_mirror pairs the two halves.  Every source
+// lane is a valid lane of the same row, so each step folds into one
+// v_max_u32_dpp.  Must run with all 16 lanes of the row active.
+#define FP8Q_DPP_MAX(v, ctrl) \
+  ({ const uint32_t o_ = uint32_t(__builtin_amdgcn_mov_dpp(int(v), (ctrl), 0xF, 0xF, true)); (v) > o_ ? (v) : o_; })
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = FP8Q_DPP_MAX(v, 0xB1);
+  v = FP8Q_DPP_MAX(v, 0x4E);
+  v = FP8Q_DPP_MAX(v, 0x141);
+  v = FP8Q_DPP_MAX(v, 0x140);
   return v;
 }
-
-// Max over a DPP quad (4 consecutive lanes), broadcast to the quad.
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = FP8Q_DPP_MAX(v, 0xB1);
+  v = FP8Q_DPP_MAX(v, 0x4E);
   return v;
 }
 
 __device__ __forceinline__ float clamp448(float v) {
   return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
 }
-
-// Four already-scaled FP32 values -> four E4M3FN bytes (a in byte 0 ... d in
-// byte 3).  The clamp makes saturation explicit; v_cvt_pk_fp8_f32 rounds to
-// nearest-even under the default FP round mode.
-__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
-}
-
-// BF16 pairs packed little-endian in a 32-bit word -> two floats (exact).
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Load 8 consecutive input elements (16-byte aligned) as floats.
-template <typename T> struct Load8;
-
-template <> struct Load8<uint16_t> {   // BF16 bit patterns
-  static __device__ __forceinline__ void run(const uint16_t* p, float (&v)[8]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-  }
-};
-
-template <> struct Load8<float> {
-  static __device__ __forceinline__ void run(const float* p, float (&v)[8]) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
 
 }  // namespace fp8q
