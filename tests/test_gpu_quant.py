@@ -218,3 +218,26 @@ def test_full_output_grad_both_tilings_sampled():
     qt_ref, s_ref = oq.quant_128x1(oq.bf16_bits_to_f32(dy[:, cols]), "pow2")
     assert_bytes_equal(host(qt)[cols], qt_ref, "128x1 codes")
     assert_bytes_equal(host(s)[:, cols], s_ref, "128x1 scales")
+
+
+@pytest.mark.parametrize("mode_name,mode", MODES)
+def test_scale_derivation_across_all_binades(mode_name, mode):
+    """262144 tiles whose max-abs values cover every float32 binade from the
+    floor 448*2^-126 to 2^127 with random mantissas (plus the exact edges); the
+    scales (and the codes, which depend on the reciprocal scale) must equal the
+    oracle's IEEE-division results bit for bit."""
+    fp8q = require_gpu()
+    rng = np.random.default_rng(101)
+    n_tiles = 262144
+    lo, hi = 0x04E00000, 0x7F7FFFFF
+    amax_bits = rng.integers(lo, hi + 1, size=n_tiles, dtype=np.int64)
+    amax_bits[:8] = [lo, lo + 1, 0x7F000000, hi, 0x43E00000, 0x3F800000, 0x7E800000, 0x72800000]
+    amax = amax_bits.astype(np.uint32).view(np.float32)
+    body = rng.uniform(-1.0, 1.0, size=(n_tiles, 128)).astype(np.float32)
+    x = (body * amax[:, None]).astype(np.float32)
+    x[:, 0] = amax
+    x = np.where(np.isfinite(x), x, 0).astype(np.float32)
+    q, s = fp8q.fp8_quant_tile(dev(x), fp8q.TILE_1x128, mode)
+    q_ref, s_ref = oq.quant_1x128(x, mode_name)
+    assert_bytes_equal(host(s), s_ref, "scales")
+    assert_bytes_equal(host(q), q_ref, "codes")
