@@ -226,28 +226,33 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     constexpr int NB = PN * 4;            // B fragments per group
     constexpr int NT = NB * SM;           // MFMAs per group
     constexpr int LAG = 2;
-    // Fragment reads run ahead of their MFMAs: A fragment ms is read one step
-    // before its first use, B fragment bi two fragments (2*SM steps) ahead.
+    // Fragment reads run ahead of their MFMAs.  The compiler only ever waits
+    // for all outstanding LDS reads (lgkmcnt(0)), so every prefetch is issued
+    // right after an MFMA, never just before a fragment's first use: the
+    // group's A fragments and B fragments 0-1 up front, then B fragment bi+2
+    // (and the next per-column scales) after the first MFMA of block bi.
     v8i af[SM];
     v8i bfb[3];
-    af[0] = read_frag(ta, wm * TM + lr, lq);
+    v4f sbq[3];                             // slot b%3: block b's scales (lagged FMAs still read b-1)
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) af[ms] = read_frag(ta, wm * TM + 16 * ms + lr, lq);
     bfb[0] = read_frag(tb, wn * TN + lr, lq);
     if (NB > 1) bfb[1] = read_frag(tb, wn * TN + 16 + lr, lq);
+    if constexpr (BSCALE == kScaleRow) sbq[0] = *reinterpret_cast<const v4f*>(tb + B_BYTES + (wn * TN + 16 * lq) * 4);
     v4f dq[3];
-    v4f sbq[2];
 #pragma unroll
     for (int t = 0; t < NT + LAG; ++t) {
       if (t < NT) {
         const int bi = t / SM, ms = t % SM;
-        if (bi == 0 && ms + 1 < SM) af[ms + 1] = read_frag(ta, wm * TM + 16 * (ms + 1) + lr, lq);
+        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        dq[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfb[bi % 3], af[ms], zero, 0, 0, 0, 0, 0, 0);
         if (ms == 0) {
           if (bi + 2 < NB) bfb[(bi + 2) % 3] = read_frag(tb, wn * TN + 16 * (bi + 2) + lr, lq);
           if constexpr (BSCALE == kScaleRow)
-            sbq[bi & 1] = *reinterpret_cast<const v4f*>(tb + B_BYTES +
-                                                       (wn * TN + 64 * (bi >> 2) + 16 * lq + 4 * (bi & 3)) * 4);
+            if (bi + 1 < NB)
+              sbq[(bi + 1) % 3] = *reinterpret_cast<const v4f*>(
+                  tb + B_BYTES + (wn * TN + 64 * ((bi + 1) >> 2) + 16 * lq + 4 * ((bi + 1) & 3)) * 4);
         }
-        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        dq[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfb[bi % 3], af[ms], zero, 0, 0, 0, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (t >= LAG) {
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
         const v4f d = dq[u % 3];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float dj = BSCALE == kScaleRow ? d[j] * sbq[bu & 1][j] : d[j];
+          const float dj = BSCALE == kScaleRow ? d[j] * sbq[bu % 3][j] : d[j];
           acc[mu][pn][js][j] = __builtin_fmaf(dj, cs[mu], acc[mu][pn][js][j]);
         }
       }
