@@ -319,12 +319,14 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
 
 // Tile configurations, largest that divides the problem:
 //   256x256, 8 waves (4 along M x 2 along N) of 64x128
-//   128x256, 4 waves (2x2) of 64x128  (also every grouped GEMM: one group per 128-row tile)
+//   128x256, 8 waves (2x4) of 64x64 for grouped GEMMs (one group per 128-row tile)
+//   128x256, 4 waves (2x2) of 64x128
 //   256x128, 4 waves (4x1) of 64x128
 //   128x128, 4 waves (2x2) of 64x64
 template <int BSCALE, int OUT, bool GROUPED>
 static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   if (!GROUPED && a.M % 256 == 0 && a.N % 256 == 0) return launch_cfg<256, 256, 4, 2, BSCALE, OUT, GROUPED>(a, st);
+  if (GROUPED && a.N % 256 == 0) return launch_cfg<128, 256, 2, 4, BSCALE, OUT, GROUPED>(a, st);
   if (a.N % 256 == 0) return launch_cfg<128, 256, 2, 2, BSCALE, OUT, GROUPED>(a, st);
   if (!GROUPED && a.M % 256 == 0) return launch_cfg<256, 128, 4, 1, BSCALE, OUT, GROUPED>(a, st);
   return launch_cfg<128, 128, 2, 2, BSCALE, OUT, GROUPED>(a, st);
