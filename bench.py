@@ -100,6 +100,7 @@ class Step:
         self.dw = e((D_OUT, D_IN), f32)
         self.my = e((self.m_pad, N_MOE), bf)
         self.pow2_q, self.pow2_s = e((T, D_IN), u8), e((D_IN // 128, T), f32)
+        self.rq_qt, self.rq_st = e((D_IN, T), u8), e((T // 128, D_IN), f32)
 
         bf16_quant_bytes = lambda r, c: r * c * 2 + r * c + (r * c // 128) * 4      # in + codes + scales
         block_bytes = lambda r, c, t: r * c * 2 + r * c * (2 if t else 1) + (r // 128) * (c // 128) * 4 * (2 if t else 1)
@@ -137,6 +138,10 @@ class Step:
             ("quant_1x128 X (pow2 scales)", lambda: q.fp8_quant_tile(self.x, q.TILE_1x128, q.POW2,
                                                                      self.pow2_q, self.pow2_s),
              bf16_quant_bytes(T, D_IN), "bytes"),
+            # consumes the pow2 codes written by the line above
+            ("requant 1x128->128x1 X (pow2 scales)", lambda: q.fp8_requant_1x128_to_128x1(
+                self.pow2_q, self.pow2_s, q.POW2, self.rq_qt, self.rq_st),
+             2 * T * D_IN + 2 * (T * D_IN // 128) * 4, "bytes"),
         ]
         self.step_flop = sum(w for _, _, w, kind in self.kernels if kind == "flop")
 
@@ -203,7 +208,7 @@ def main():
         us = float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)])) * 1e3
         per_kernel[name] = _kernel_entry(us, work, kind)
 
-    # extra kernels outside the step (pow2 scale mode of the activation quantizer)
+    # extra kernels outside the step (pow2 scale mode of the activation quantizer, FP8 re-tiling)
     for name, fn, work, kind in step.extra:
         for _ in range(2):
             fn()

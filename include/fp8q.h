@@ -175,6 +175,36 @@ int fp8_gemm_blockscaled_grouped(int32_t num_groups, int64_t M_total, int64_t N,
                                  void* c, int c_dtype, int64_t ldc,
                                  void* stream);
 
+/*
+ * fp8_requant_1x128_to_128x1 -- FP8 -> FP8 re-tiling of 1x128-quantized
+ * activations into 128x1 tiles for the backward pass, without a trip through
+ * BF16.  [dssusan.co.kr FP8 excerpt, paragraph 4: 1x128 tiles converted to
+ * 128x1 tiles in backward; paragraph 1: power-of-2 scales for these
+ * activations]
+ *
+ * q        : input codes Q[rows][cols] (E4M3 bytes, 1x128 tiles), leading
+ *            dimension ld_q (bytes).
+ * scales   : their 1x128 scales, scales[cols/128][rows], packed (exactly what
+ *            fp8_quant_tile(..., FP8Q_TILE_1x128, ...) writes).
+ * mode     : scale rule of the OUTPUT tiles, FP8Q_SCALE_POW2 or MAXABS.
+ * q_t      : output codes, TRANSPOSED: q_t[cols][rows], leading dimension
+ *            ld_qt (bytes); q_t[c*ld_qt + r] is the new code of element (r, c).
+ * scales_t : output scales[rows/128][cols], packed (the 128x1 layout of
+ *            fp8_quant_tile).
+ * Computes, for every element, xh = fl32(dec(Q[r][c]) * scales[c/128][r])
+ * (exact when the input scales are powers of two) and quantizes xh with the
+ * quantization rule above over each 128x1 group (128 rows of one column).
+ * With power-of-2 scales on both sides, a column whose 128x1 scale equals
+ * every row's 1x128 scale comes back with its codes unchanged.
+ * Input codes must not be NaN (0x7F / 0xFF): unspecified output.
+ * Requires rows % 128 == 0 and cols % 128 == 0.
+ * rows == 0 or cols == 0 is a no-op returning FP8Q_OK.
+ */
+int fp8_requant_1x128_to_128x1(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q,
+                               const float* scales, int mode,
+                               uint8_t* q_t, int64_t ld_qt, float* scales_t,
+                               void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8q_status_string(int status);
 

@@ -160,3 +160,28 @@ def dequant_128x128(q, s):
     r, c = q.shape
     full = np.repeat(np.repeat(np.asarray(s, np.float64), GROUP, axis=0), GROUP, axis=1)
     return e4m3.decode(q) * full[:r, :c]
+
+
+def requant_1x128_to_128x1(q, s, mode=MODE_POW2):
+    """FP8 -> FP8 re-tiling: 1x128 codes Q[R][C] with scales S[C/128][R] to
+    128x1 tiles, output transposed.
+
+    The backward pass converts cached activations from 1x128 tiles to 128x1
+    tiles (dssusan.co.kr FP8 excerpt, paragraph 4), and those activations use
+    power-of-2 scales (paragraph 1).  Steps, in the pages' order:
+      1. dequantize each element in float32: xh = fl32(dec(Q[r][c]) * S[c/128][r])
+         (exact when S is a power of 2);
+      2. quantize xh in 128x1 tiles exactly as ``quant_128x1`` does.
+    Returns QT[C][R] (uint8) and S'[ceil(R/128)][C] (float32).
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    r, c = q.shape
+    s = np.asarray(s, dtype=np.float32)
+    if s.shape != (_ceil(c, GROUP), r):
+        raise ValueError("1x128 scales must be shaped [ceil(C/128)][R]")
+    dec = e4m3.decode(q).astype(np.float32)                  # exact: E4M3 values fit float32
+    if not np.all(np.isfinite(dec)):
+        raise ValueError("NaN codes are not defined for the re-quantizer")
+    col_scale = np.repeat(s.T, GROUP, axis=1)[:, :c]         # [R][C] float32
+    xh = (dec * col_scale).astype(np.float32)                # one float32 rounding
+    return quant_128x1(xh, mode)

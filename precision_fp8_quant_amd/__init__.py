@@ -11,6 +11,7 @@ Functions keep the C names:
     fp8_quant_block(w, mode, transposed)       -> (q, scales[, q_t, scales_t])
     fp8_gemm_blockscaled(kind, a, sa, b, sb)   -> c
     fp8_gemm_blockscaled_grouped(gmap, a, sa, b, sb) -> c
+    fp8_requant_1x128_to_128x1(q, scales, mode) -> (q_t, scales_t)
 FP8 tensors are torch.uint8 holding OCP E4M3FN codes.
 """
 
@@ -42,6 +43,7 @@ SIGNATURES = {
                              _int, _ptr],
     "fp8_gemm_blockscaled_grouped": [_i32, _i64, _i64, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _int,
                                      _i64, _ptr],
+    "fp8_requant_1x128_to_128x1": [_ptr, _i64, _i64, _i64, _ptr, _int, _ptr, _i64, _ptr, _ptr],
     "fp8q_status_string": [_int],
     "fp8q_abi_version": [],
 }
@@ -196,3 +198,19 @@ def fp8_gemm_blockscaled_grouped(group_of_mtile, a, a_scales, b, b_scales, out_d
                                             a_scales.data_ptr(), b.data_ptr(), b_scales.data_ptr(),
                                             c.data_ptr(), _dtype_code(c), _ld(c), _stream(stream)))
     return c
+
+
+def fp8_requant_1x128_to_128x1(q, scales, mode=POW2, q_t=None, scales_t=None, stream=None):
+    """FP8 -> FP8 re-tiling of 1x128 codes q[rows][cols] (scales[cols/128][rows]) into
+    128x1 tiles: q_t[cols][rows] transposed, scales_t[rows/128][cols]."""
+    q = _codes(_rowmajor(q, "q"))
+    rows, cols = q.shape
+    dev = q.device
+    if q_t is None:
+        q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if scales_t is None:
+        scales_t = torch.empty((rows // 128, cols), dtype=torch.float32, device=dev)
+    q_t = _codes(q_t)
+    _check(lib.fp8_requant_1x128_to_128x1(q.data_ptr(), rows, cols, _ld(q), scales.data_ptr(), mode,
+                                          q_t.data_ptr(), _ld(q_t), scales_t.data_ptr(), _stream(stream)))
+    return q_t, scales_t

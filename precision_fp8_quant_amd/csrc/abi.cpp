@@ -35,7 +35,7 @@ int from_hip(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_HIP; }
 
 extern "C" {
 
-int fp8q_abi_version(void) { return 100; }
+int fp8q_abi_version(void) { return 101; }
 
 const char* fp8q_status_string(int s) {
   switch (s) {
@@ -113,6 +113,29 @@ int fp8_quant_block(const void* w, int w_dtype, int64_t rows, int64_t cols, int6
   }
   return from_hip(fp8q::launch_quant_128x128(w, w_dtype == FP8Q_BF16, rows, cols, ld_w, mode, q, ld_q,
                                              scales, q_t, ld_qt, scales_t,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fp8_requant_1x128_to_128x1(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q,
+                               const float* scales, int mode,
+                               uint8_t* q_t, int64_t ld_qt, float* scales_t, void* stream) {
+  if (mode != FP8Q_SCALE_MAXABS && mode != FP8Q_SCALE_POW2) return FP8Q_ERR_ARG;
+  if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8Q_OK;
+  if (!q || !scales || !q_t || !scales_t) return FP8Q_ERR_NULL;
+  if (ld_q < cols || ld_qt < rows) return FP8Q_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(scales) || !aligned16(q_t) || !aligned16(scales_t) || ld_q % 16 ||
+      ld_qt % 16)
+    return FP8Q_ERR_ALIGN;
+  if (rows % 128 || cols % 128) return FP8Q_ERR_UNSUPPORTED;
+  const int64_t nscale = (rows / 128) * cols;   // same count on both sides
+  const Range ins[2] = {span(q, rows, cols, ld_q, 1), span(scales, 1, nscale, nscale, 4)};
+  const Range outs[2] = {span(q_t, cols, rows, ld_qt, 1), span(scales_t, 1, nscale, nscale, 4)};
+  if (overlap(outs[0], outs[1])) return FP8Q_ERR_ALIAS;
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
+      if (overlap(ins[i], outs[j])) return FP8Q_ERR_ALIAS;
+  return from_hip(fp8q::launch_requant_128x1(q, rows, cols, ld_q, scales, mode, q_t, ld_qt, scales_t,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 

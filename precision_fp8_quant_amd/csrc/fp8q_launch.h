@@ -18,6 +18,9 @@ hipError_t launch_quant_128x128(const void* w, bool bf16, int64_t rows, int64_t 
                                 int mode, uint8_t* q, int64_t ld_q, float* scales,
                                 uint8_t* q_t, int64_t ld_qt, float* scales_t, hipStream_t st);
 
+hipError_t launch_requant_128x1(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q, const float* s_in,
+                                int mode, uint8_t* q_t, int64_t ld_qt, float* s_out, hipStream_t st);
+
 // kind: 0 Fprop, 1 Dgrad (block-scaled B), 2 Wgrad (per-row B scales)
 hipError_t launch_gemm(int kind, int64_t M, int64_t N, int64_t K,
                        const uint8_t* a, int64_t lda, const float* sa,

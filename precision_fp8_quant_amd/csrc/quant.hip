@@ -21,6 +21,7 @@ namespace fp8q {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Eight consecutive elements as raw 32-bit words: 4 words of BF16 pairs, or
 // 8 words of FP32.
@@ -299,6 +300,102 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// FP8 -> FP8 re-tiling of 1x128 codes into 128x1 tiles (output transposed),
+// the backward-pass conversion of cached activations: dssusan.co.kr FP8
+// excerpt, paragraph 4 (with power-of-2 scales, paragraph 1).  A workgroup
+// handles a 128-row x 128-column tile, i.e. exactly one 1x128 group per row.
+// Thread t holds rows 4*(t/8)..+3 of the 16 columns 16*(t%8)..+15.
+//   1. 16-byte code loads, one 16-byte load of its 4 row scales; decode with
+//      v_cvt_pk_f32_fp8 and dequantize in FP32 (exact for power-of-2 scales)
+//   2. column max on the bits of |x|: 4 rows in registers, lanes t and t+8
+//      via DPP row_ror:8, 16 partials per column through LDS
+//   3. threads 0..127 finish one column each (scale pair, store s, publish inv)
+//   4. scale + cast; each column's 4 rows pack into one dword, staged in an
+//      LDS tile T[col][row] (pitch 132 bytes); thread t then copies 64 bytes
+//      of column t/2 (rows 64*(t%2)..+63) to the output.
+// ---------------------------------------------------------------------------
+constexpr int kRqPartPitch = 132;   // dwords per LDS row of column partials
+
+template <int MODE>
+__global__ __launch_bounds__(256) void requant_128x1_kernel(
+    const uint8_t* __restrict__ q, int64_t rows, int64_t cols, int64_t ld_q,
+    const float* __restrict__ s_in, uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ s_out) {
+  __shared__ uint32_t part[16 * kRqPartPitch];
+  __shared__ float inv_s[128];
+  __shared__ uint32_t tile[128 * kT1Pitch / 4];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int c8 = t & 7;
+  const int q4 = t >> 3;
+  const int64_t ctiles = cols >> 7;
+  const int64_t tiles = ctiles * (rows >> 7);
+  for (int64_t u = blockIdx.x; u < tiles; u += gridDim.x) {   // block-uniform: barriers stay matched
+  const int64_t cg = u % ctiles;
+  const int64_t rblk = u / ctiles;
+  const int64_t row0 = rblk * 128;
+  const int64_t col0 = cg * 128;
+
+  u32x4 w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = *reinterpret_cast<const u32x4*>(q + (row0 + q4 * 4 + j) * ld_q + col0 + c8 * 16);
+  const v4f sr = *reinterpret_cast<const v4f*>(s_in + cg * rows + row0 + q4 * 4);
+
+  float x[4][16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[j][d]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[j][d]), true);
+      x[j][4 * d + 0] = lo[0] * sr[j];
+      x[j][4 * d + 1] = lo[1] * sr[j];
+      x[j][4 * d + 2] = hi[0] * sr[j];
+      x[j][4 * d + 3] = hi[1] * sr[j];
+    }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t b = __float_as_uint(x[j][i]) & 0x7FFFFFFFu;
+      m = b > m ? b : m;
+    }
+    m = FP8Q_DPP_MAX(m, 0x128);                   // row_ror:8 -> lanes l and l+8 of a DPP row
+    if ((lane & 15) < 8) part[((t >> 6) * 4 + ((lane >> 4) & 3)) * kRqPartPitch + c8 * 16 + i] = m;
+  }
+  __syncthreads();
+  if (t < 128) {
+    uint32_t m = part[t];
+#pragma unroll
+    for (int p = 1; p < 16; ++p) {
+      const uint32_t b = part[p * kRqPartPitch + t];
+      m = b > m ? b : m;
+    }
+    const ScalePair sp = scale_from_amax_bits<MODE>(m);
+    inv_s[t] = sp.inv;
+    s_out[rblk * cols + col0 + t] = sp.s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float inv = inv_s[c8 * 16 + i];
+    tile[((c8 * 16 + i) * kT1Pitch + q4 * 4) >> 2] = cvt4<MODE>(x[0][i], x[1][i], x[2][i], x[3][i], inv);
+  }
+  __syncthreads();
+  const int cc = t >> 1;
+  const int hh = t & 1;
+  const uint32_t* src = tile + ((cc * kT1Pitch + hh * 64) >> 2);
+  uint8_t* dst = q_t + (col0 + cc) * ld_qt + row0 + hh * 64;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    reinterpret_cast<u32x4*>(dst)[k] = u32x4{src[4 * k], src[4 * k + 1], src[4 * k + 2], src[4 * k + 3]};
+  __syncthreads();                                // LDS is reused by the next tile
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (shapes already validated by the ABI layer).
 // ---------------------------------------------------------------------------
 #define FP8Q_DISPATCH(KERNEL, bf16, mode, grid, st, ...)                                  \
@@ -352,5 +449,17 @@ hipError_t launch_quant_128x128(const void* x_, bool bf16, int64_t rows, int64_t
 }
 
 #undef FP8Q_DISPATCH
+
+hipError_t launch_requant_128x1(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q, const float* s_in,
+                                int mode, uint8_t* q_t, int64_t ld_qt, float* s_out, hipStream_t st) {
+  const dim3 grid(unit_grid((cols / 128) * (rows / 128)));
+  if (mode == kModePow2)
+    hipLaunchKernelGGL((requant_128x1_kernel<kModePow2>), grid, dim3(256), 0, st, q, rows, cols, ld_q, s_in,
+                       q_t, ld_qt, s_out);
+  else
+    hipLaunchKernelGGL((requant_128x1_kernel<kModeMaxAbs>), grid, dim3(256), 0, st, q, rows, cols, ld_q, s_in,
+                       q_t, ld_qt, s_out);
+  return hipGetLastError();
+}
 
 }  // namespace fp8q

@@ -28,7 +28,8 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert names == {"fp8_quant_tile", "fp8_quant_block", "fp8_gemm_blockscaled",
-                     "fp8_gemm_blockscaled_grouped", "fp8q_status_string", "fp8q_abi_version"}
+                     "fp8_gemm_blockscaled_grouped", "fp8_requant_1x128_to_128x1", "fp8q_status_string",
+                     "fp8q_abi_version"}
     raw = ctypes.CDLL(fp8q.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -36,7 +37,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert fp8q.lib.fp8q_abi_version() == 100
+    assert fp8q.lib.fp8q_abi_version() == 101
     for s in range(8):
         assert fp8q.status_string(s).startswith("FP8Q_")
     assert fp8q.status_string(99) == "unknown fp8q status"
@@ -134,3 +135,27 @@ def test_grouped_validation():
 def test_binding_raises_on_error_status():
     with pytest.raises(fp8q.Fp8qError):
         fp8q._check(fp8q.ERR_SHAPE)
+
+
+def _requant(**kw):
+    args = dict(q=A, rows=256, cols=384, ldq=384, s=B, mode=fp8q.POW2, qt=C, ldqt=256, st=D)
+    args.update(kw)
+    return fp8q.lib.fp8_requant_1x128_to_128x1(args["q"], args["rows"], args["cols"], args["ldq"], args["s"],
+                                               args["mode"], args["qt"], args["ldqt"], args["st"], None)
+
+
+def test_requant_validation():
+    assert _requant(rows=0, q=None) == fp8q.OK
+    assert _requant(mode=3) == fp8q.ERR_ARG
+    assert _requant(cols=-128) == fp8q.ERR_SHAPE
+    for k in ("q", "s", "qt", "st"):
+        assert _requant(**{k: None}) == fp8q.ERR_NULL
+    assert _requant(ldq=256) == fp8q.ERR_SHAPE
+    assert _requant(ldqt=128) == fp8q.ERR_SHAPE
+    assert _requant(q=A + 8) == fp8q.ERR_ALIGN
+    assert _requant(ldq=392) == fp8q.ERR_ALIGN
+    assert _requant(rows=200, ldqt=208) == fp8q.ERR_UNSUPPORTED
+    assert _requant(cols=200, ldq=208) == fp8q.ERR_UNSUPPORTED
+    assert _requant(qt=A + 256) == fp8q.ERR_ALIAS          # codes out over codes in
+    assert _requant(st=C + 1024) == fp8q.ERR_ALIAS         # scales out inside codes out
+    assert _requant(st=B) == fp8q.ERR_ALIAS                # scales out over scales in

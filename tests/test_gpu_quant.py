@@ -241,3 +241,90 @@ def test_scale_derivation_across_all_binades(mode_name, mode):
     q_ref, s_ref = oq.quant_1x128(x, mode_name)
     assert_bytes_equal(host(s), s_ref, "scales")
     assert_bytes_equal(host(q), q_ref, "codes")
+
+
+# ----------------------------------------------------------------------------
+# FP8 -> FP8 1x128 -> 128x1 re-quantization.  Every input (codes and scales)
+# comes from the oracle's 1x128 quantizer or from a seeded generator.
+# ----------------------------------------------------------------------------
+
+def _requant_check(fp8q, q, s, mode_name, mode):
+    qt, st = fp8q.fp8_requant_1x128_to_128x1(dev(q), dev(s), mode)
+    qt_ref, st_ref = oq.requant_1x128_to_128x1(q, s, mode_name)
+    assert_bytes_equal(host(qt), qt_ref, "transposed codes")
+    assert_bytes_equal(host(st), st_ref, "128x1 scales")
+
+
+@pytest.mark.parametrize("in_mode", ["maxabs", "pow2"])
+@pytest.mark.parametrize("mode_name,mode", MODES)
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 256), (1024, 128)])
+def test_requant_from_oracle_1x128(in_mode, mode_name, mode, shape):
+    fp8q = require_gpu()
+    q, s = oq.quant_1x128(_data(sum(shape) + 7, shape), in_mode)
+    _requant_check(fp8q, q, s, mode_name, mode)
+
+
+@pytest.mark.parametrize("mode_name,mode", MODES)
+def test_requant_every_code_and_extreme_scales(mode_name, mode):
+    # Every finite code (both zeros and all subnormals included) under row
+    # scales spread from 2^-126 to 2^100, power-of-2 and not, so the FP32
+    # dequantization runs through subnormal and huge products.
+    fp8q = require_gpu()
+    rng = np.random.default_rng(31)
+    rows, cols = 512, 512
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    q = rng.choice(finite, size=(rows, cols)).astype(np.uint8)
+    e = rng.integers(-126, 101, size=(cols // 128, rows))
+    mant = np.where(rng.random((cols // 128, rows)) < 0.5, 1.0, rng.uniform(1.0, 2.0, (cols // 128, rows)))
+    s = (mant * np.exp2(e.astype(np.float64))).astype(np.float32)
+    s[0, :4] = [2.0 ** -126, np.float32(1.5 * 2.0 ** -126), 2.0 ** 100, np.float32(1.0 / 448.0)]
+    _requant_check(fp8q, q, s, mode_name, mode)
+
+
+def test_requant_lossless_when_scales_align():
+    fp8q = require_gpu()
+    rng = np.random.default_rng(32)
+    rows, cols = 256, 256
+    q = rng.integers(0, 0x78, size=(rows, cols), dtype=np.uint8) | (rng.integers(0, 2, (rows, cols)) << 7).astype(np.uint8)
+    q[rng.integers(0, 128, cols), np.arange(cols)] = 0x7E          # every 128x1 tile reaches 448
+    q[128 + rng.integers(0, 128, cols), np.arange(cols)] = 0xF8    # ... and -256
+    s = np.full((cols // 128, rows), 2.0 ** -5, dtype=np.float32)
+    qt, st = fp8q.fp8_requant_1x128_to_128x1(dev(q), dev(s), 1)
+    assert_bytes_equal(host(qt), np.ascontiguousarray(q.T), "codes come back transposed and unchanged")
+    assert np.all(host(st) == np.float32(2.0 ** -5))
+
+
+def test_requant_strided_input_and_output():
+    fp8q = require_gpu()
+    q, s = oq.quant_1x128(_data(33, (256, 256)), "pow2")
+    q_big = torch.zeros((256, 384), dtype=torch.uint8, device="cuda")
+    q_big[:, :256] = dev(q)
+    qt_big = torch.full((256, 320), 0xAB, dtype=torch.uint8, device="cuda")
+    st = torch.empty((2, 256), dtype=torch.float32, device="cuda")
+    fp8q.fp8_requant_1x128_to_128x1(q_big[:, :256], dev(s), 1, q_t=qt_big[:, :256], scales_t=st)
+    qt_ref, st_ref = oq.requant_1x128_to_128x1(q, s, "pow2")
+    h = host(qt_big)
+    assert_bytes_equal(h[:, :256], qt_ref, "codes")
+    assert np.all(h[:, 256:] == 0xAB), "padding columns of the output were written"
+    assert_bytes_equal(host(st), st_ref, "scales")
+
+
+@pytest.fixture(scope="module")
+def activation_pow2_1x128(layer):
+    d, _, _ = layer
+    return oq.quant_1x128(oq.bf16_bits_to_f32(d["x"]), "pow2")
+
+
+@pytest.mark.parametrize("mode_name,mode", MODES)
+def test_full_requant_activation_sampled_groups(activation_pow2_1x128, mode_name, mode):
+    # 8192 x 7168 activation, 1x128 pow2 codes as the backward pass caches
+    # them; three 128-column groups are recomputed by the oracle.
+    fp8q = require_gpu()
+    q, s = activation_pow2_1x128
+    qt, st = fp8q.fp8_requant_1x128_to_128x1(dev(q), dev(s), mode)
+    qth, sth = host(qt), host(st)
+    for g in (0, 29, 55):
+        cs = slice(g * 128, (g + 1) * 128)
+        qt_ref, st_ref = oq.requant_1x128_to_128x1(np.ascontiguousarray(q[:, cs]), s[g:g + 1], mode_name)
+        assert_bytes_equal(qth[cs], qt_ref, f"group {g} codes")
+        assert_bytes_equal(sth[:, cs], st_ref, f"group {g} scales")

@@ -75,3 +75,27 @@ def test_dropped_integer_rescale_is_caught(monkeypatch):
     monkeypatch.setattr(gemm, "_PAIR_SCALE", 2.0 ** -9)
     with pytest.raises(AssertionError):
         pins_gemm.test_unit_scales_equal_plain_product()
+
+
+def _requant_without_dequant(q, s, mode=quant.MODE_POW2):
+    return quant.quant_128x1(e4m3.decode(np.asarray(q, np.uint8)).astype(np.float32), mode)
+
+
+def _requant_wrong_group_scale(q, s, mode=quant.MODE_POW2):
+    s = np.asarray(s, np.float32)
+    return ORIG_REQUANT(q, np.roll(s, 1, axis=0), mode)
+
+
+ORIG_REQUANT = quant.requant_1x128_to_128x1
+
+
+def test_requant_without_dequantization_is_caught(monkeypatch):
+    monkeypatch.setattr(quant, "requant_1x128_to_128x1", _requant_without_dequant)
+    with pytest.raises(AssertionError):
+        pins_quant.test_requant_scale_covariance(quant.MODE_POW2)
+
+
+def test_requant_with_another_groups_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(quant, "requant_1x128_to_128x1", _requant_wrong_group_scale)
+    with pytest.raises(AssertionError):
+        pins_quant.test_requant_error_bound_against_source(quant.MODE_POW2)

@@ -223,3 +223,79 @@ def test_tiny_config_quantization_shapes():
     qb, sb = quant.quant_128x128(d["bt"])
     assert qa.shape == (128, 256) and sa.shape == (2, 128)
     assert qb.shape == (128, 256) and sb.shape == (1, 2)
+
+
+# ---------------------------------------------------------------------------
+# FP8 -> FP8 1x128 -> 128x1 re-quantization (dssusan.co.kr FP8 excerpt,
+# paragraph 4 for the conversion, paragraph 1 for its power-of-2 scales).
+# ---------------------------------------------------------------------------
+
+def _codes_with_big_entry_per_column_tile(seed, r, c):
+    """Random finite codes where every 128x1 column tile holds one |dec| in (224, 448]."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 256, size=(r, c), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] ^= 0x01                           # no NaN codes
+    q[(q & 0x7F) > 0x77] &= 0xF7                            # |dec| <= 224 everywhere ...
+    for g in range(r // 128):
+        rows = g * 128 + rng.integers(0, 128, size=c)
+        q[rows, np.arange(c)] = rng.choice([0x78, 0x7A, 0x7E, 0xF9, 0xFE], size=c)   # ... but one > 224
+    return q
+
+
+def test_requant_is_lossless_when_row_scales_align():
+    # Every row scale 2^e and every column tile reaching (224, 448]*2^e: the
+    # 128x1 tiles get the same scale 2^e and the codes come back unchanged,
+    # only transposed (pow2 scales make the re-quantization exact).
+    r, c = 256, 384
+    q = _codes_with_big_entry_per_column_tile(11, r, c)
+    for e in (-20, 0, 7):
+        s = np.full((c // 128, r), 2.0 ** e, dtype=np.float32)
+        qt, st = quant.requant_1x128_to_128x1(q, s, quant.MODE_POW2)
+        assert np.array_equal(qt, q.T)
+        assert np.all(st == np.float32(2.0 ** e))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_requant_scale_covariance(mode):
+    # Multiplying every input scale by 2^j multiplies every output scale by
+    # 2^j and leaves the codes alone (both scale rules are invariant under
+    # exact power-of-two rescaling away from under/overflow).
+    x = _outlier_data(12, (256, 256))
+    q, s = quant.quant_1x128(x, mode)
+    qt0, st0 = quant.requant_1x128_to_128x1(q, s, mode)
+    for j in (-9, 5):
+        qt1, st1 = quant.requant_1x128_to_128x1(q, (s * np.float32(2.0 ** j)).astype(np.float32), mode)
+        assert np.array_equal(qt1, qt0)
+        assert np.array_equal(st1, (st0 * np.float32(2.0 ** j)).astype(np.float32))
+
+
+def test_requant_maxabs_maps_column_max_to_448():
+    x = _outlier_data(13, (256, 384))
+    q, s = quant.quant_1x128(x, quant.MODE_POW2)
+    qt, st = quant.requant_1x128_to_128x1(q, s, quant.MODE_MAXABS)
+    d = np.abs(e4m3.decode(qt)).reshape(384, 2, 128).max(axis=2)
+    xh = np.abs(e4m3.decode(q) * np.repeat(s.T, 128, axis=1)).T.reshape(384, 2, 128).max(axis=2)
+    assert np.all(d[xh > 0] == 448.0)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_requant_error_bound_against_source(mode):
+    # Two roundings, each at most half an E4M3 step of its own tile:
+    # |dec(q')s' - x| <= |dec(q)s - x| + 2^-4 |xh| + 2^-10 s'  (E4M3 keeps 3
+    # mantissa bits; the subnormal step is 2^-9 of the tile scale).
+    x = _outlier_data(14, (256, 256))
+    q, s = quant.quant_1x128(x, quant.MODE_POW2)
+    xh = quant.dequant_1x128(q, s)
+    qt, st = quant.requant_1x128_to_128x1(q, s, mode)
+    back = e4m3.decode(qt).T * np.repeat(st.astype(np.float64), 128, axis=0)
+    bound = np.abs(xh - x) + np.abs(xh) * 2.0 ** -4 + np.repeat(st.astype(np.float64), 128, axis=0) * 2.0 ** -10
+    assert np.all(np.abs(back - x) <= bound)
+
+
+def test_requant_rejects_wrong_scale_shape_and_nan_codes():
+    q = np.zeros((128, 256), dtype=np.uint8)
+    with pytest.raises(ValueError):
+        quant.requant_1x128_to_128x1(q, np.ones((1, 128), np.float32))
+    q[5, 7] = 0x7F
+    with pytest.raises(ValueError):
+        quant.requant_1x128_to_128x1(q, np.ones((2, 128), np.float32))
