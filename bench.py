@@ -59,7 +59,7 @@ def parse():
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("quant.hip", "gemm.hip", "fp8q_device.h"):
+    for f in ("quant.hip", "gemm.hip", "gemm_kernel.h", "gemm_pow2.hip", "fp8q_device.h"):
         with open(os.path.join(ROOT, "precision_fp8_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -101,6 +101,8 @@ class Step:
         self.my = e((self.m_pad, N_MOE), bf)
         self.pow2_q, self.pow2_s = e((T, D_IN), u8), e((D_IN // 128, T), f32)
         self.rq_qt, self.rq_st = e((D_IN, T), u8), e((T // 128, D_IN), f32)
+        self.qw_p2, self.sw_p2 = e((D_OUT, D_IN), u8), e((D_OUT // 128, D_IN // 128), f32)
+        self.qdyt_p2, self.sdyt_p2 = e((D_OUT, T), u8), e((T // 128, D_OUT), f32)
 
         bf16_quant_bytes = lambda r, c: r * c * 2 + r * c + (r * c // 128) * 4      # in + codes + scales
         block_bytes = lambda r, c, t: r * c * 2 + r * c * (2 if t else 1) + (r // 128) * (c // 128) * 4 * (2 if t else 1)
@@ -142,6 +144,19 @@ class Step:
             ("requant 1x128->128x1 X (pow2 scales)", lambda: q.fp8_requant_1x128_to_128x1(
                 self.pow2_q, self.pow2_s, q.POW2, self.rq_qt, self.rq_st),
              2 * T * D_IN + 2 * (T * D_IN // 128) * 4, "bytes"),
+            # power-of-two operands for the hardware-scaled MFMA GEMMs (outputs reuse y / dW)
+            ("quant_128x128 W (pow2 scales)", lambda: q.fp8_quant_block(self.wt, q.POW2, False, self.qw_p2,
+                                                                       self.sw_p2),
+             block_bytes(D_OUT, D_IN, False), "bytes"),
+            ("gemm Fprop pow2 (hardware-scaled MFMA)", lambda: q.fp8_gemm_blockscaled_pow2(
+                q.FPROP, self.pow2_q, self.pow2_s, self.qw_p2, self.sw_p2, c=self.y),
+             gf(T, D_OUT, D_IN), "flop"),
+            ("quant_128x1 dY (pow2 scales)", lambda: q.fp8_quant_tile(self.dy, q.TILE_128x1, q.POW2, self.qdyt_p2,
+                                                                      self.sdyt_p2),
+             bf16_quant_bytes(T, D_OUT), "bytes"),
+            ("gemm Wgrad pow2 (hardware-scaled MFMA)", lambda: q.fp8_gemm_blockscaled_pow2(
+                q.WGRAD, self.qdyt_p2, self.sdyt_p2, self.rq_qt, self.rq_st, c=self.dw),
+             gf(D_OUT, D_IN, T), "flop"),
         ]
         self.step_flop = sum(w for _, _, w, kind in self.kernels if kind == "flop")
 
@@ -208,7 +223,7 @@ def main():
         us = float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)])) * 1e3
         per_kernel[name] = _kernel_entry(us, work, kind)
 
-    # extra kernels outside the step (pow2 scale mode of the activation quantizer, FP8 re-tiling)
+    # extra kernels outside the step, in order (power-of-two scale mode, FP8 re-tiling, hardware-scaled GEMMs)
     for name, fn, work, kind in step.extra:
         for _ in range(2):
             fn()

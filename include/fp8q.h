@@ -151,6 +151,27 @@ int fp8_gemm_blockscaled(int kind, int64_t M, int64_t N, int64_t K,
                          void* stream);
 
 /*
+ * fp8_gemm_blockscaled_pow2 -- the same GEMM for operands whose scales are
+ * all integral powers of two (FP8Q_SCALE_POW2 quantizer output), with the
+ * group scaling done by the matrix cores themselves.
+ * [dssusan.co.kr FP8 excerpt, paragraph 1: power-of-2 scales; paragraph 3 and
+ *  "Deepseek - Not For everyone", paragraph 4: MMA with group scaling]
+ *
+ * Arguments, layouts, shape rules and status codes are exactly those of
+ * fp8_gemm_blockscaled.  Each scale is handed to gfx950's
+ * v_mfma_scale_f32_16x16x128_f8f6f4 as an E8M0 code (its biased exponent), so
+ * every 128-deep group is dequantized inside the MFMA and accumulated in the
+ * MFMA's own FP32 accumulator across all K-groups: there is no per-group VALU
+ * promotion.  Only the exponent field of each scale is used: a scale that is
+ * not a positive power of two in [2^-126, 2^127] gives unspecified output.
+ */
+int fp8_gemm_blockscaled_pow2(int kind, int64_t M, int64_t N, int64_t K,
+                              const uint8_t* a, int64_t lda, const float* a_scales,
+                              const uint8_t* b, int64_t ldb, const float* b_scales,
+                              void* c, int c_dtype, int64_t ldc, int accumulate,
+                              void* stream);
+
+/*
  * fp8_gemm_blockscaled_grouped -- grouped (MoE expert) Fprop.
  * [dssusan.co.kr FP8 excerpt, paragraph 3 and "Deepseek - Not For everyone",
  *  paragraph 4 for the scaling; MoE experts per "Deepseek - Not For everyone",

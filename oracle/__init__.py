@@ -26,6 +26,9 @@ Modules:
     quant  -- 1x128, 128x1 and 128x128 quantizers, max-abs and pow2 modes (all pinned).
     gemm   -- block-scaled GEMM reference for Fprop/Dgrad/Wgrad and the grouped
               variant, plus output rounding to FP32/BF16 (all pinned).
+    study  -- quantization-error study of the scaling rules (per-tensor,
+              1x128, 128x128, power-of-2, delayed), built on the pinned
+              quantizers; ``python -m oracle.study`` prints the table.
 """
 
 from . import e4m3, quant, gemm  # noqa: F401

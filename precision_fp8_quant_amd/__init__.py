@@ -10,6 +10,7 @@ Functions keep the C names:
     fp8_quant_tile(x, tile, mode)              -> (q, scales)
     fp8_quant_block(w, mode, transposed)       -> (q, scales[, q_t, scales_t])
     fp8_gemm_blockscaled(kind, a, sa, b, sb)   -> c
+    fp8_gemm_blockscaled_pow2(kind, a, sa, b, sb)   -> c   (power-of-two scales)
     fp8_gemm_blockscaled_grouped(gmap, a, sa, b, sb) -> c
     fp8_requant_1x128_to_128x1(q, scales, mode) -> (q_t, scales_t)
 FP8 tensors are torch.uint8 holding OCP E4M3FN codes.
@@ -41,6 +42,8 @@ SIGNATURES = {
     "fp8_quant_block": [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr],
     "fp8_gemm_blockscaled": [_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _int, _i64,
                              _int, _ptr],
+    "fp8_gemm_blockscaled_pow2": [_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _int, _i64,
+                                  _int, _ptr],
     "fp8_gemm_blockscaled_grouped": [_i32, _i64, _i64, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _int,
                                      _i64, _ptr],
     "fp8_requant_1x128_to_128x1": [_ptr, _i64, _i64, _i64, _ptr, _int, _ptr, _i64, _ptr, _ptr],
@@ -164,6 +167,16 @@ def fp8_quant_block(w, mode=MAXABS, transposed=False, q=None, scales=None, q_t=N
 def fp8_gemm_blockscaled(kind, a, a_scales, b, b_scales, out_dtype=torch.bfloat16, c=None,
                          accumulate=False, stream=None):
     """C[M][N] (+)= A . B^T with per-128-K-group scales (see include/fp8q.h)."""
+    return _gemm(lib.fp8_gemm_blockscaled, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream)
+
+
+def fp8_gemm_blockscaled_pow2(kind, a, a_scales, b, b_scales, out_dtype=torch.bfloat16, c=None,
+                              accumulate=False, stream=None):
+    """Same GEMM for power-of-two scales, applied by the hardware-scaled MFMA."""
+    return _gemm(lib.fp8_gemm_blockscaled_pow2, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream)
+
+
+def _gemm(fn, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream):
     a, b = _codes(_rowmajor(a, "a")), _codes(_rowmajor(b, "b"))
     m, k = a.shape
     n = b.shape[0]
@@ -172,9 +185,8 @@ def fp8_gemm_blockscaled(kind, a, a_scales, b, b_scales, out_dtype=torch.bfloat1
     if c is None:
         c = torch.empty((m, n), dtype=out_dtype, device=a.device)
     _rowmajor(c, "c")
-    _check(lib.fp8_gemm_blockscaled(kind, m, n, k, a.data_ptr(), _ld(a), a_scales.data_ptr(),
-                                    b.data_ptr(), _ld(b), b_scales.data_ptr(), c.data_ptr(),
-                                    _dtype_code(c), _ld(c), 1 if accumulate else 0, _stream(stream)))
+    _check(fn(kind, m, n, k, a.data_ptr(), _ld(a), a_scales.data_ptr(), b.data_ptr(), _ld(b), b_scales.data_ptr(),
+              c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0, _stream(stream)))
     return c
 
 

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libfp8q.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-DEVICE_SOURCES = ["quant.hip", "gemm.hip"]
+DEVICE_SOURCES = ["quant.hip", "gemm.hip", "gemm_pow2.hip"]
 HOST_SOURCES = ["abi.cpp"]
 
 # -ffp-contract=off: the quantizer's scale-multiply-then-round sequence must be
@@ -25,10 +25,12 @@ HOST_SOURCES = ["abi.cpp"]
 # back); the GEMM asks for its FMAs explicitly.
 # -packed-fp32-ops off: keep the compiler from forming packed FP32 VALU ops.
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-I", INCLUDE, "-I", CSRC]
-# -amdgpu-mfma-vgpr-form: MFMA results go straight to VGPRs, where the FP32
-# promotion FMAs read them (no v_accvgpr_read copies).
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-unused-command-line-argument"]
+                "-Wno-unused-command-line-argument"]
+# -amdgpu-mfma-vgpr-form: MFMA results go straight to VGPRs, where the FP32
+# promotion FMAs read them (no v_accvgpr_read copies).  Not for the
+# hardware-scaled GEMM, whose accumulators stay in AGPRs inside the MFMA chain.
+PER_SOURCE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd, verbose):
@@ -46,7 +48,8 @@ def build(verbose=False, extra_flags=()):
     jobs = []
     for src in DEVICE_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append([HIPCC, *COMMON_FLAGS, *DEVICE_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *COMMON_FLAGS, *DEVICE_FLAGS, *PER_SOURCE_FLAGS.get(src, []), *extra_flags,
+                     "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         jobs.append([HIPCC, *COMMON_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])

@@ -35,7 +35,7 @@ int from_hip(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_HIP; }
 
 extern "C" {
 
-int fp8q_abi_version(void) { return 101; }
+int fp8q_abi_version(void) { return 102; }
 
 const char* fp8q_status_string(int s) {
   switch (s) {
@@ -139,14 +139,19 @@ int fp8_requant_1x128_to_128x1(const uint8_t* q, int64_t rows, int64_t cols, int
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
-int fp8_gemm_blockscaled(int kind, int64_t M, int64_t N, int64_t K,
-                         const uint8_t* a, int64_t lda, const float* a_scales,
-                         const uint8_t* b, int64_t ldb, const float* b_scales,
-                         void* c, int c_dtype, int64_t ldc, int accumulate, void* stream) {
+// Shared validation of the two plain GEMM entry points; on success the
+// caller launches.
+static int check_gemm(int kind, int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                      const float* a_scales, const uint8_t* b, int64_t ldb, const float* b_scales, void* c,
+                      int c_dtype, int64_t ldc, int accumulate, bool* nothing_to_do) {
+  *nothing_to_do = false;
   if (kind != FP8Q_FPROP && kind != FP8Q_DGRAD && kind != FP8Q_WGRAD) return FP8Q_ERR_ARG;
   if (!dtype_ok(c_dtype) || (accumulate != 0 && accumulate != 1)) return FP8Q_ERR_ARG;
   if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
-  if (M == 0 || N == 0) return FP8Q_OK;
+  if (M == 0 || N == 0) {
+    *nothing_to_do = true;
+    return FP8Q_OK;
+  }
   if (!c) return FP8Q_ERR_NULL;
   if (K > 0 && (!a || !b || !a_scales || !b_scales)) return FP8Q_ERR_NULL;
   if (ldc < N || (K > 0 && (lda < K || ldb < K))) return FP8Q_ERR_SHAPE;
@@ -165,9 +170,33 @@ int fp8_gemm_blockscaled(int kind, int64_t M, int64_t N, int64_t K,
                         span(a_scales, 1, nsa, nsa, 4), span(b_scales, 1, nsb, nsb, 4)};
   for (int i = 0; i < 4; ++i)
     if (overlap(rc, ins[i])) return FP8Q_ERR_ALIAS;
+  return FP8Q_OK;
+}
+
+int fp8_gemm_blockscaled(int kind, int64_t M, int64_t N, int64_t K,
+                         const uint8_t* a, int64_t lda, const float* a_scales,
+                         const uint8_t* b, int64_t ldb, const float* b_scales,
+                         void* c, int c_dtype, int64_t ldc, int accumulate, void* stream) {
+  bool nothing = false;
+  const int st = check_gemm(kind, M, N, K, a, lda, a_scales, b, ldb, b_scales, c, c_dtype, ldc, accumulate,
+                            &nothing);
+  if (st != FP8Q_OK || nothing) return st;
   return from_hip(fp8q::launch_gemm(kind, M, N, K, a, lda, a_scales, b, ldb, b_scales, c,
                                     c_dtype == FP8Q_BF16, ldc, accumulate != 0,
                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fp8_gemm_blockscaled_pow2(int kind, int64_t M, int64_t N, int64_t K,
+                              const uint8_t* a, int64_t lda, const float* a_scales,
+                              const uint8_t* b, int64_t ldb, const float* b_scales,
+                              void* c, int c_dtype, int64_t ldc, int accumulate, void* stream) {
+  bool nothing = false;
+  const int st = check_gemm(kind, M, N, K, a, lda, a_scales, b, ldb, b_scales, c, c_dtype, ldc, accumulate,
+                            &nothing);
+  if (st != FP8Q_OK || nothing) return st;
+  return from_hip(fp8q::launch_gemm_pow2(kind, M, N, K, a, lda, a_scales, b, ldb, b_scales, c,
+                                         c_dtype == FP8Q_BF16, ldc, accumulate != 0,
+                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
 int fp8_gemm_blockscaled_grouped(int32_t num_groups, int64_t M_total, int64_t N, int64_t K,

@@ -1,0 +1,433 @@
+// Block-scaled FP8 GEMMs for gfx950: Fprop, Dgrad, Wgrad and grouped Fprop.
+//
+//   C[m][n] = sum_g  sa(g,m) * sb(g,n) * P_g[m][n],
+//   P_g[m][n] = sum_{k in K-group g} dec(A[m][k]) * dec(B[n][k])
+//
+// Per-group scales along K, multiplied in as the dequantization step, with
+// the partial products promoted to FP32 accumulation once per group:
+// dssusan.co.kr FP8 excerpt, paragraph 3; "Deepseek - Not For everyone",
+// paragraph 4; youlimart.com FP8 excerpt, paragraphs 2 and 3.
+//
+// CDNA4 mapping.  One v_mfma_f32_16x16x128_f8f6f4 consumes exactly one
+// 128-deep K-group of a 16x16 output tile, so every MFMA result is a complete
+// group partial P_g for its tile: it is produced with a zero accumulator and
+// folded into the FP32 accumulators by one VALU FMA per element with the
+// combined scale.  The promotion interval is therefore one K-group (128).
+//
+// The MFMA is issued "swapped": the B fragment (16 rows of N) is source A and
+// the A fragment (16 rows of M) is source B, so a lane's four results lie in
+// one row m and four columns n.  The 16 rows of each B fragment are drawn from
+// a 64-column panel in the order n = 16*(r/4) + 4*js + r%4 (js = subtile),
+// which leaves every lane with 16 consecutive columns of one output row after
+// the four subtiles of a panel: 32-byte (BF16) or 64-byte (FP32) row runs.
+//
+// Data path per K-group: global -> LDS by LDS DMA (global_load_lds_dwordx4,
+// issued one group ahead into the other of two stages; 16-byte chunks
+// XOR-swizzled by row) -> ds_read_b128 fragments -> MFMA -> FMA into FP32
+// accumulators.
+//
+// The same template with HW=true is the hardware-scaled variant for
+// power-of-two scales: v_mfma_scale_f32_16x16x128_f8f6f4 receives the A-row
+// and B-row/block scales as E8M0 exponents and accumulates every group in
+// place, so the loop carries no VALU work (instantiated in gemm_pow2.hip).
+#pragma once
+
+#include "fp8q_launch.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+enum { kScaleBlock = 0, kScaleRow = 1 };   // B scales: 128x128 blocks, or per-row (128x1 tiles)
+enum { kOutBF16 = 0, kOutF32 = 1, kOutF32Acc = 2 };
+
+struct GemmArgs {
+  const uint8_t* a; int64_t lda; const float* sa;
+  const uint8_t* b; int64_t ldb; const float* sb;
+  void* c; int64_t ldc;
+  int64_t M, N, K;
+  // grouped variant
+  const int32_t* group_of_mtile; int32_t num_groups; int64_t b_group_stride; int64_t sb_group_stride;
+};
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// LDS tile rows are 128 bytes (one K-group) in eight 16-byte chunks; chunk c
+// of row r is stored at position c ^ (r & 7).  The K order inside one MFMA
+// is free as long as both operands use the same one, so lane quarter q
+// (lanes 16q..16q+15) feeds its fragment from chunks q and q+4.  The LDS
+// serves a ds_read_b128 in four passes of 16 lanes -- lanes whose 4-lane
+// group index has even / odd bit parity, per half-wave -- over 64 four-byte
+// banks (256 bytes); with this chunk assignment and swizzle every pass of both
+// fragment reads touches 16 distinct 16-byte bank groups (no conflicts),
+// while the DMA still moves whole 128-byte rows.
+__device__ __forceinline__ int swz(int row) { return row & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
+
+// B tiles are stored in LDS in fragment order: LDS row rho = 64*p + 16*js + r
+// holds global row 64*p + 16*(r/4) + 4*js + r%4, so the 16 rows a fragment
+// needs are consecutive in LDS while a lane still ends up owning 16
+// consecutive output columns.
+__device__ __forceinline__ int b_row_of_lds_row(int rho) {
+  return (rho & ~63) | (((rho & 15) >> 2) << 4) | (((rho >> 4) & 3) << 2) | (rho & 3);
+}
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// 16 bytes per lane from global memory straight into LDS at dst + 16*lane
+// (dst is wave-uniform).  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+}
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+  return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lq) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + lds_off(row, lq));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + lds_off(row, lq + 4));
+  return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+}
+
+template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, bool HW>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM;          // wave tile rows (M)
+  constexpr int TN = BN / WN;          // wave tile cols (N)
+  constexpr int SM = TM / 16;          // M subtiles per wave
+  constexpr int PN = TN / 64;          // 64-column panels per wave
+  static_assert(TM % 16 == 0 && TN % 64 == 0, "wave tile shape");
+  static_assert(BSCALE == kScaleRow || 128 % TN == 0, "block-scaled B needs a wave inside one 128-column block");
+  constexpr int A_BYTES = BM * 128;
+  constexpr int B_BYTES = BN * 128;
+  constexpr int SB_BYTES = BSCALE == kScaleRow ? BN * 4 : 0;   // one group's per-column B scales
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int SB_SLOTS = 2;           // per-column B scales of groups g and g+1, beside the stages
+  constexpr int A_DMA = A_BYTES / 1024 / NW;     // 1 KB wave-wide DMA instructions per wave per stage
+  constexpr int B_DMA = B_BYTES / 1024 / NW;
+  static_assert(A_DMA * 1024 * NW == A_BYTES && B_DMA * 1024 * NW == B_BYTES, "DMA split");
+  static_assert(BN <= 256, "row scales: one DMA of at most 64 lanes x 4 floats");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + SB_SLOTS * SB_BYTES];
+  uint8_t* const sb_ring = smem + 2 * STAGE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  // ---- tile scheduling: XCD-aware remap, then grouped-M ordering ----------
+  const int64_t tiles_m = p.M / BM;
+  const int64_t tiles_n = p.N / BN;
+  const int64_t ntiles = tiles_m * tiles_n;
+  int64_t bid = blockIdx.x;
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);   // neighbouring tiles share an XCD
+  constexpr int64_t GROUP_M = 8;
+  const int64_t per_group = GROUP_M * tiles_n;
+  const int64_t first_m = (bid / per_group) * GROUP_M;
+  const int64_t gsize = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+  const int64_t mt = first_m + (bid % per_group) % gsize;
+  const int64_t nt = (bid % per_group) / gsize;
+  const int64_t m0 = mt * BM;
+  const int64_t n0 = nt * BN;
+
+  const uint8_t* bptr = p.b;
+  const float* sbptr = p.sb;
+  if constexpr (GROUPED) {
+    const int32_t grp = p.group_of_mtile[mt];
+    if (grp < 0 || grp >= p.num_groups) return;     // block-uniform, before any barrier
+    bptr += int64_t(grp) * p.b_group_stride;
+    sbptr += int64_t(grp) * p.sb_group_stride;
+  }
+  const int64_t KG = p.K >> 7;
+
+  // ---- DMA addressing ------------------------------------------------------
+  // Wave-wide DMA instruction `blk` fills LDS rows 8*blk .. 8*blk+7; lane l
+  // lands at row 8*blk + l/8, physical chunk l%8, i.e. logical chunk
+  // (l%8) ^ swz(row) = (l%8) ^ (l/8).  The per-lane byte offset is the same
+  // for every blk and everything else is wave-uniform (SGPRs).  For B the LDS
+  // row rho maps to global row 64*(blk/8) + 32*(blk&1) + 4*((blk/2)&3)
+  // [uniform] + 16*(l/32) + (l/8)%4 [per lane].
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int lchunk = ((lane & 7) ^ (lane >> 3)) << 4;
+  const uint32_t a_off = uint32_t((lane >> 3) * p.lda + lchunk);
+  const uint32_t b_off = uint32_t((16 * (lane >> 5) + ((lane >> 3) & 3)) * p.ldb + lchunk);
+  const uint8_t* a_base = p.a + m0 * p.lda;
+  const uint8_t* b_base = bptr + n0 * p.ldb;
+
+  // The wave-uniform part of every DMA source address goes through
+  // readfirstlane, so it stays in SGPRs and is recomputed per group (saddr +
+  // 32-bit voffset form) instead of being hoisted out of the loop as one
+  // 64-bit VGPR pair per DMA instruction.
+  auto issue_stage = [&](int64_t g, int stage) {
+    uint8_t* base = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+      const int blk = wave_u * A_DMA + i;
+      dma16(uniform_ptr(a_base + int64_t(8 * blk) * p.lda + g * 128) + a_off, base + blk * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+      const int blk = wave_u * B_DMA + i;
+      const int row_u = 64 * (blk >> 3) + 32 * (blk & 1) + 4 * ((blk >> 1) & 3);
+      dma16(uniform_ptr(b_base + int64_t(row_u) * p.ldb + g * 128) + b_off, base + A_BYTES + blk * 1024);
+    }
+  };
+  // Per-column B scales of group g into slot `slot` (issued at the top of an
+  // iteration, where a wave-uniform branch splits no MFMA/FMA block).
+  auto issue_scales = [&](int64_t g, int slot) {
+    if constexpr (BSCALE == kScaleRow) {
+      if (wave_u == NW - 1 && lane < BN / 4)
+        dma16(uniform_ptr(reinterpret_cast<const uint8_t*>(sbptr + g * p.N + n0)) + lane * 16,
+              sb_ring + slot * SB_BYTES);
+    }
+  };
+
+  // ---- per-lane output coordinates ----------------------------------------
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int64_t m_lane = m0 + wm * TM + lr;                 // + 16*ms
+  const int64_t n_wave = n0 + wn * TN;                      // + 64*pn + 16*lq + 4*js + j
+
+  // Promoted path: FP32 accumulators updated by VALU FMAs once per group.
+  // Hardware-scaled path (HW): the MFMA applies both power-of-two scales
+  // itself and accumulates every group into accv (no VALU work at all).
+  float acc[SM][PN][4][4];
+  v4f accv[SM][PN][4];
+#pragma unroll
+  for (int a = 0; a < SM; ++a)
+#pragma unroll
+    for (int b = 0; b < PN; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (HW) accv[a][b][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc[a][b][c][d] = 0.0f;
+      }
+
+  // Per K-group: the DMA of group g+1 into the other stage is issued first,
+  // then the group's MFMAs run from LDS fragments, then one barrier.  Inside
+  // the group a software pipeline over its NT = NB*SM MFMAs (step t: B
+  // fragment bi = t/SM against A fragment ms = t%SM):
+  //  * promoted path: MFMA t writes result slot t%3 and the promotion FMAs of
+  //    MFMA t-2 follow it, so a VALU op never waits on the MFMA just issued;
+  //  * hardware-scaled path (HW): the MFMA takes both E8M0 scales and
+  //    accumulates in place; nothing else runs;
+  //  * fragment reads run ahead of their MFMAs: the group's A fragments and B
+  //    fragments 0-1 up front, then B fragment bi+2 (with the per-column
+  //    Wgrad scales it needs) right after the first MFMA of block bi.  The
+  //    compiler only ever waits for all outstanding LDS reads (lgkmcnt(0)), so
+  //    every prefetch is issued right after an MFMA, never just before a
+  //    fragment's first use.
+  // A scheduling barrier after every step pins this interleave (left alone,
+  // the compiler places each FMA right behind its own MFMA and pads the
+  // hazard with s_nop).
+  constexpr int NB = PN * 4;            // B fragments per group
+  constexpr int NT = NB * SM;           // MFMAs per group
+  constexpr int LAG = HW ? 0 : 2;
+  static_assert(!(HW && GROUPED), "the hardware-scaled path covers the plain GEMMs");
+
+  auto frag_row_b = [&](int bi) { return wn * TN + 16 * bi + lr; };
+  auto sbq_off = [&](int bi) { return (wn * TN + 64 * (bi >> 2) + 16 * lq + 4 * (bi & 3)) * 4; };
+  // HW: the source-A row this lane feeds in B fragment bi is the LDS row
+  // frag_row_b(bi), i.e. tile column wn*TN + 64*(bi/4) + 16*(lr/4) + 4*(bi%4) + lr%4.
+  // A power-of-two float's E8M0 code is its biased exponent field.
+  auto sbe_read = [&](const uint8_t* ring, int bi) {
+    const int col = wn * TN + 64 * (bi >> 2) + 16 * (lr >> 2) + 4 * (bi & 3) + (lr & 3);
+    return reinterpret_cast<const uint32_t*>(ring)[col] >> 23;
+  };
+
+  float sa_cur[SM], sa_nxt[SM];
+  float sb_cur = 0.0f, sb_nxt = 0.0f;
+  if (KG > 0) {
+    issue_stage(0, 0);
+    issue_scales(0, 0);
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) sa_cur[ms] = p.sa[m_lane + 16 * ms];
+    if constexpr (BSCALE == kScaleBlock) sb_cur = sbptr[(n_wave >> 7) * KG];
+    wait_vmem_all();
+  }
+  __syncthreads();
+
+  // One basic block per iteration (no branches between the MFMAs and their
+  // promotion FMAs): the last iteration simply re-fetches its own group into
+  // the idle stage, which nobody reads.
+  for (int64_t g = 0; g < KG; ++g) {
+    const int stage = int(g & 1);
+    const int64_t gn = g + 1 < KG ? g + 1 : g;
+    issue_stage(gn, stage ^ 1);
+    issue_scales(gn, stage ^ 1);
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) sa_nxt[ms] = p.sa[gn * p.M + m_lane + 16 * ms];
+    if constexpr (BSCALE == kScaleBlock) sb_nxt = sbptr[(n_wave >> 7) * KG + gn];
+
+    const uint8_t* ta = smem + stage * STAGE;
+    const uint8_t* tb = ta + A_BYTES;
+    const uint8_t* ts = sb_ring + stage * SB_BYTES;
+    float cs[SM];
+    uint32_t sae[SM];                                   // HW: E8M0 codes of the A-row scales
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) {
+      cs[ms] = BSCALE == kScaleBlock ? sa_cur[ms] * sb_cur : sa_cur[ms];
+      sae[ms] = __float_as_uint(sa_cur[ms]) >> 23;
+    }
+    const uint32_t sbe_blk = __float_as_uint(sb_cur) >> 23;
+
+    v8i af[SM];
+    v8i bfb[3];
+    v4f sbq[3];                             // promoted Wgrad: slot b%3 holds block b's column scales
+    uint32_t sbe[3];                        // HW Wgrad: slot b%3 holds this lane's B-row E8M0 code
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) af[ms] = read_frag(ta, wm * TM + 16 * ms + lr, lq);
+    bfb[0] = read_frag(tb, frag_row_b(0), lq);
+    if (NB > 1) bfb[1] = read_frag(tb, frag_row_b(1), lq);
+    if constexpr (BSCALE == kScaleRow) {
+      if constexpr (HW) {
+        sbe[0] = sbe_read(ts, 0);
+        if (NB > 1) sbe[1] = sbe_read(ts, 1);
+      } else {
+        sbq[0] = *reinterpret_cast<const v4f*>(ts + sbq_off(0));
+      }
+    }
+    v4f dq[3];
+#pragma unroll
+    for (int t = 0; t < NT + LAG; ++t) {
+      if (t < NT) {
+        const int bi = t / SM, ms = t % SM;
+        if constexpr (HW) {
+          // v_mfma_scale_f32_16x16x128_f8f6f4: E8M0 scale of source A (this
+          // lane's B row) and of source B (this lane's A row) applied in the
+          // matrix core, result accumulated in place
+          const uint32_t sb_e = BSCALE == kScaleRow ? sbe[bi % 3] : sbe_blk;
+          accv[ms][bi >> 2][bi & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bfb[bi % 3], af[ms], accv[ms][bi >> 2][bi & 3], 0, 0, 0, sb_e, 0, sae[ms]);
+        } else {
+          const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+          dq[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfb[bi % 3], af[ms], zero, 0, 0, 0, 0, 0, 0);
+        }
+        if (ms == 0) {
+          if (bi + 2 < NB) {
+            bfb[(bi + 2) % 3] = read_frag(tb, frag_row_b(bi + 2), lq);
+            if constexpr (HW && BSCALE == kScaleRow) sbe[(bi + 2) % 3] = sbe_read(ts, bi + 2);
+          }
+          if constexpr (!HW && BSCALE == kScaleRow)
+            if (bi + 1 < NB) sbq[(bi + 1) % 3] = *reinterpret_cast<const v4f*>(ts + sbq_off(bi + 1));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (!HW && t >= LAG) {
+        const int u = t - LAG;
+        const int bu = u / SM, mu = u % SM;
+        const int pn = bu >> 2, js = bu & 3;
+        const v4f d = dq[u % 3];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float dj = BSCALE == kScaleRow ? d[j] * sbq[bu % 3][j] : d[j];
+          acc[mu][pn][js][j] = __builtin_fmaf(dj, cs[mu], acc[mu][pn][js][j]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep step t's MFMA and step t-2's FMAs together
+    }
+#pragma unroll
+    for (int ms = 0; ms < SM; ++ms) sa_cur[ms] = sa_nxt[ms];
+    sb_cur = sb_nxt;
+    wait_vmem_all();
+    __syncthreads();
+  }
+  if constexpr (HW) {
+#pragma unroll
+    for (int a = 0; a < SM; ++a)
+#pragma unroll
+      for (int b = 0; b < PN; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) acc[a][b][c][d] = accv[a][b][c][d];
+  }
+
+  // ---- epilogue: each lane writes 16 consecutive columns of SM*PN rows ----
+#pragma unroll
+  for (int ms = 0; ms < SM; ++ms) {
+    const int64_t m = m_lane + 16 * ms;
+#pragma unroll
+    for (int pn = 0; pn < PN; ++pn) {
+      const int64_t n = n_wave + 64 * pn + 16 * lq;
+      if constexpr (OUT == kOutBF16) {
+        uint32_t w[8];
+#pragma unroll
+        for (int js = 0; js < 4; ++js) {
+          w[2 * js] = bf16_rne_bits(acc[ms][pn][js][0]) | (bf16_rne_bits(acc[ms][pn][js][1]) << 16);
+          w[2 * js + 1] = bf16_rne_bits(acc[ms][pn][js][2]) | (bf16_rne_bits(acc[ms][pn][js][3]) << 16);
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + m * p.ldc + n);
+        dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+        dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+      } else {
+        v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.c) + m * p.ldc + n);
+#pragma unroll
+        for (int js = 0; js < 4; ++js) {
+          v4f o = {acc[ms][pn][js][0], acc[ms][pn][js][1], acc[ms][pn][js][2], acc[ms][pn][js][3]};
+          if constexpr (OUT == kOutF32Acc) o += dst[js];
+          dst[js] = o;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch configurations.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, bool HW>
+static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
+  const int64_t tiles = (a.M / BM) * (a.N / BN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WM, WN, BSCALE, OUT, GROUPED, HW>),
+                     dim3(unsigned(tiles)), dim3(WM * WN * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+// Tile configurations, largest that divides the problem:
+//   256x256, 8 waves (4 along M x 2 along N) of 64x128
+//   128x256, 8 waves (2x4) of 64x64 for grouped GEMMs (one group per 128-row tile)
+//   128x256, 4 waves (2x2) of 64x128
+//   256x128, 4 waves (4x1) of 64x128
+//   128x128, 4 waves (2x2) of 64x64
+template <int BSCALE, int OUT, bool GROUPED, bool HW>
+static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
+  if (!GROUPED && a.M % 256 == 0 && a.N % 256 == 0) return launch_cfg<256, 256, 4, 2, BSCALE, OUT, GROUPED, HW>(a, st);
+  if (GROUPED && a.N % 256 == 0) return launch_cfg<128, 256, 2, 4, BSCALE, OUT, GROUPED, HW>(a, st);
+  if (a.N % 256 == 0) return launch_cfg<128, 256, 2, 2, BSCALE, OUT, GROUPED, HW>(a, st);
+  if (!GROUPED && a.M % 256 == 0) return launch_cfg<256, 128, 4, 1, BSCALE, OUT, GROUPED, HW>(a, st);
+  return launch_cfg<128, 128, 2, 2, BSCALE, OUT, GROUPED, HW>(a, st);
+}
+
+template <int BSCALE, bool GROUPED, bool HW>
+static hipError_t launch_out(const GemmArgs& a, int out, hipStream_t st) {
+  switch (out) {
+    case kOutBF16: return launch_tiles<BSCALE, kOutBF16, GROUPED, HW>(a, st);
+    case kOutF32: return launch_tiles<BSCALE, kOutF32, GROUPED, HW>(a, st);
+    default: return launch_tiles<BSCALE, kOutF32Acc, GROUPED, HW>(a, st);
+  }
+}
+
+static int out_code(bool out_bf16, bool accumulate) {
+  return out_bf16 ? kOutBF16 : (accumulate ? kOutF32Acc : kOutF32);
+}
+
+}  // namespace fp8q

@@ -28,7 +28,8 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert names == {"fp8_quant_tile", "fp8_quant_block", "fp8_gemm_blockscaled",
-                     "fp8_gemm_blockscaled_grouped", "fp8_requant_1x128_to_128x1", "fp8q_status_string",
+                     "fp8_gemm_blockscaled_grouped", "fp8_requant_1x128_to_128x1",
+                     "fp8_gemm_blockscaled_pow2", "fp8q_status_string",
                      "fp8q_abi_version"}
     raw = ctypes.CDLL(fp8q.LIB_PATH)
     for n in names:
@@ -37,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert fp8q.lib.fp8q_abi_version() == 101
+    assert fp8q.lib.fp8q_abi_version() == 102
     for s in range(8):
         assert fp8q.status_string(s).startswith("FP8Q_")
     assert fp8q.status_string(99) == "unknown fp8q status"
@@ -89,29 +90,30 @@ def test_quant_block_validation():
     assert _block(qt=B + 16, ldqt=256, st=D) == fp8q.ERR_ALIAS  # transposed codes overlap codes
 
 
-def _gemm(**kw):
+def _gemm(fn="fp8_gemm_blockscaled", **kw):
     args = dict(kind=fp8q.FPROP, M=256, N=256, K=512, a=A, lda=512, sa=B, b=C, ldb=512, sb=D,
                 c=0x7000000, cdt=fp8q.BF16, ldc=256, acc=0)
     args.update(kw)
-    return fp8q.lib.fp8_gemm_blockscaled(args["kind"], args["M"], args["N"], args["K"], args["a"], args["lda"],
+    return getattr(fp8q.lib, fn)(args["kind"], args["M"], args["N"], args["K"], args["a"], args["lda"],
                                          args["sa"], args["b"], args["ldb"], args["sb"], args["c"], args["cdt"],
                                          args["ldc"], args["acc"], None)
 
 
-def test_gemm_validation():
-    assert _gemm(M=0) == fp8q.OK
-    assert _gemm(kind=3) == fp8q.ERR_ARG
-    assert _gemm(cdt=4) == fp8q.ERR_ARG
-    assert _gemm(acc=2) == fp8q.ERR_ARG
-    assert _gemm(K=-128) == fp8q.ERR_SHAPE
-    assert _gemm(c=None) == fp8q.ERR_NULL
-    assert _gemm(sb=None) == fp8q.ERR_NULL
-    assert _gemm(lda=256) == fp8q.ERR_SHAPE
-    assert _gemm(ldc=200) == fp8q.ERR_SHAPE
-    assert _gemm(b=C + 8) == fp8q.ERR_ALIGN
-    assert _gemm(M=200) == fp8q.ERR_UNSUPPORTED
-    assert _gemm(acc=1) == fp8q.ERR_UNSUPPORTED                  # accumulate needs FP32 output
-    assert _gemm(c=A + 4096) == fp8q.ERR_ALIAS
+@pytest.mark.parametrize("fn", ["fp8_gemm_blockscaled", "fp8_gemm_blockscaled_pow2"])
+def test_gemm_validation(fn):
+    assert _gemm(fn, M=0) == fp8q.OK
+    assert _gemm(fn, kind=3) == fp8q.ERR_ARG
+    assert _gemm(fn, cdt=4) == fp8q.ERR_ARG
+    assert _gemm(fn, acc=2) == fp8q.ERR_ARG
+    assert _gemm(fn, K=-128) == fp8q.ERR_SHAPE
+    assert _gemm(fn, c=None) == fp8q.ERR_NULL
+    assert _gemm(fn, sb=None) == fp8q.ERR_NULL
+    assert _gemm(fn, lda=256) == fp8q.ERR_SHAPE
+    assert _gemm(fn, ldc=200) == fp8q.ERR_SHAPE
+    assert _gemm(fn, b=C + 8) == fp8q.ERR_ALIGN
+    assert _gemm(fn, M=200) == fp8q.ERR_UNSUPPORTED
+    assert _gemm(fn, acc=1) == fp8q.ERR_UNSUPPORTED              # accumulate needs FP32 output
+    assert _gemm(fn, c=A + 4096) == fp8q.ERR_ALIAS
 
 
 def _grouped(**kw):

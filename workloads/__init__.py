@@ -129,12 +129,13 @@ def moe_layer(seed=5, groups=64, tokens=65536, d_in=7168, d_out=2048, zipf_s=1.1
             "group_of_mtile": gmap}
 
 
-def random_fp8_operands(seed, m, n, k, kind="fprop", scale_lo=2.0 ** -12, scale_hi=2.0 ** -2):
+def random_fp8_operands(seed, m, n, k, kind="fprop", scale_lo=2.0 ** -12, scale_hi=2.0 ** -2, pow2=False):
     """Random non-NaN E4M3 codes and positive float32 scales for direct GEMM tests.
 
     Codes are uniform over the 254 non-NaN bytes; scales are log-uniform in
-    [scale_lo, scale_hi]. Scale layouts: sa [K/128][M]; sb [N/128][K/128]
-    (fprop/dgrad) or [K/128][N] (wgrad).
+    [scale_lo, scale_hi] (pow2=True: their exponents rounded to integers, so
+    every scale is a power of two). Scale layouts: sa [K/128][M]; sb
+    [N/128][K/128] (fprop/dgrad) or [K/128][N] (wgrad).
     """
     rng = np.random.default_rng(seed)
     valid = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
@@ -142,9 +143,10 @@ def random_fp8_operands(seed, m, n, k, kind="fprop", scale_lo=2.0 ** -12, scale_
     qb = valid[rng.integers(0, valid.size, size=(n, k))]
     g = -(-k // GROUP)
     lo, hi = np.log2(scale_lo), np.log2(scale_hi)
-    sa = np.exp2(rng.uniform(lo, hi, size=(g, m))).astype(np.float32)
+    expo = (lambda e: np.rint(e)) if pow2 else (lambda e: e)
+    sa = np.exp2(expo(rng.uniform(lo, hi, size=(g, m)))).astype(np.float32)
     if kind == "wgrad":
-        sb = np.exp2(rng.uniform(lo, hi, size=(g, n))).astype(np.float32)
+        sb = np.exp2(expo(rng.uniform(lo, hi, size=(g, n)))).astype(np.float32)
     else:
-        sb = np.exp2(rng.uniform(lo, hi, size=(-(-n // GROUP), g))).astype(np.float32)
+        sb = np.exp2(expo(rng.uniform(lo, hi, size=(-(-n // GROUP), g)))).astype(np.float32)
     return {"qa": qa, "sa": sa, "qb": qb, "sb": sb}
