@@ -89,12 +89,6 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 __device__ __forceinline__ void dma16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
 }
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
-  return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
-}
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lq) {
@@ -170,22 +164,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   const uint8_t* a_base = p.a + m0 * p.lda;
   const uint8_t* b_base = bptr + n0 * p.ldb;
 
-  // The wave-uniform part of every DMA source address goes through
-  // readfirstlane, so it stays in SGPRs and is recomputed per group (saddr +
-  // 32-bit voffset form) instead of being hoisted out of the loop as one
-  // 64-bit VGPR pair per DMA instruction.
   auto issue_stage = [&](int64_t g, int stage) {
     uint8_t* base = smem + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
       const int blk = wave_u * A_DMA + i;
-      dma16(uniform_ptr(a_base + int64_t(8 * blk) * p.lda + g * 128) + a_off, base + blk * 1024);
+      dma16(a_base + int64_t(8 * blk) * p.lda + g * 128 + a_off, base + blk * 1024);
     }
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
       const int blk = wave_u * B_DMA + i;
       const int row_u = 64 * (blk >> 3) + 32 * (blk & 1) + 4 * ((blk >> 1) & 3);
-      dma16(uniform_ptr(b_base + int64_t(row_u) * p.ldb + g * 128) + b_off, base + A_BYTES + blk * 1024);
+      dma16(b_base + int64_t(row_u) * p.ldb + g * 128 + b_off, base + A_BYTES + blk * 1024);
     }
   };
   // Per-column B scales of group g into slot `slot` (issued at the top of an
@@ -193,8 +183,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   auto issue_scales = [&](int64_t g, int slot) {
     if constexpr (BSCALE == kScaleRow) {
       if (wave_u == NW - 1 && lane < BN / 4)
-        dma16(uniform_ptr(reinterpret_cast<const uint8_t*>(sbptr + g * p.N + n0)) + lane * 16,
-              sb_ring + slot * SB_BYTES);
+        dma16(sbptr + g * p.N + n0 + lane * 4, sb_ring + slot * SB_BYTES);
     }
   };
 
