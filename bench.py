@@ -17,6 +17,12 @@ value = useful GEMM FLOP of the step (padding rows excluded) / step time, in
 TFLOP/s; every kernel of the step is inside the timed region.  Per-kernel
 durations come from HIP events recorded on the stream the kernels run on.
 
+After the timed steps, kernels outside the step are timed one by one (their
+entries carry "outside_step"): the power-of-two scale mode of the activation
+and weight quantizers, the FP8 -> FP8 1x128 -> 128x1 re-quantization of the
+activation, and the Fprop and Wgrad GEMMs on power-of-two operands through
+the hardware-scaled MFMA path.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--copy-calibration]
 """
