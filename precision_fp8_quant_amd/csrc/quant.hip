@@ -77,11 +77,12 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d, flo
 }
 
 // ---------------------------------------------------------------------------
-// 1x128: a workgroup is 4 waves; wave w quantizes group (4*blockIdx.y + w) of
-// 16 consecutive rows starting at 16*blockIdx.x.  A 16-lane DPP row holds one
+// 1x128: a workgroup is 4 waves; a work unit is 32 consecutive rows x 4
+// groups, wave w taking group 4*stripe + w.  A 16-lane DPP row holds one
 // 128-element tile row (8 elements per lane), so the four DPP rows of a wave
-// cover 4 rows per step and 4 unrolled steps cover 16 rows.  All loads are
-// issued before any reduction.  FULL: all 16 rows exist (no row masking).
+// cover 4 rows per step and 8 unrolled steps cover 32 rows.  All eight loads
+// are issued before any reduction (32 rows measured ~2% faster than 16 on the
+// 8192x7168 activation).  FULL: all 32 rows exist (no row masking).
 // ---------------------------------------------------------------------------
 template <typename T, int MODE, bool FULL>
 __device__ __forceinline__ void quant_1x128_body(const T* __restrict__ x, int64_t rows, int64_t ld_x,
@@ -89,15 +90,15 @@ __device__ __forceinline__ void quant_1x128_body(const T* __restrict__ x, int64_
                                                  float* __restrict__ scales, int64_t g, int64_t row0,
                                                  int sub, int seg) {
   const int64_t col = g * 128 + seg * 8;
-  Raw8<T> v[4];
+  Raw8<T> v[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int64_t r = row0 + i * 4 + sub;
     if (FULL || r < rows) v[i].load(x + r * ld_x + col);
     else v[i].zero();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const ScalePair sp = scale_from_amax_bits<MODE>(row16_max_u32(v[i].amax_bits()));
     const int64_t r = row0 + i * 4 + sub;
     uint2 out;
@@ -114,18 +115,18 @@ template <typename T, int MODE>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scales) {
-  // Work units of 16 rows x 4 groups in row-band-major order, so that
+  // Work units of 32 rows x 4 groups in row-band-major order, so that
   // concurrently running workgroups stream whole rows (grid-stride loop).
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t groups = cols >> 7;
   const int64_t stripes = (groups + 3) >> 2;
-  const int64_t units = ((rows + 15) >> 4) * stripes;
+  const int64_t units = ((rows + 31) >> 5) * stripes;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
     const int64_t g = (u % stripes) * 4 + wave;
-    const int64_t row0 = (u / stripes) * 16;
+    const int64_t row0 = (u / stripes) * 32;
     if (g >= groups) continue;                   // wave-uniform; this kernel has no barriers
-    if (row0 + 16 <= rows)
+    if (row0 + 32 <= rows)
       quant_1x128_body<T, MODE, true>(x, rows, ld_x, q, ld_q, scales, g, row0, lane >> 4, lane & 15);
     else
       quant_1x128_body<T, MODE, false>(x, rows, ld_x, q, ld_q, scales, g, row0, lane >> 4, lane & 15);
@@ -427,7 +428,7 @@ static unsigned unit_grid(int64_t units) {
 
 hipError_t launch_quant_1x128(const void* x_, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
                               int mode, uint8_t* q, int64_t ld_q, float* scales, hipStream_t st) {
-  const dim3 grid(unit_grid(((rows + 15) / 16) * ((cols / 128 + 3) / 4)));
+  const dim3 grid(unit_grid(((rows + 31) / 32) * ((cols / 128 + 3) / 4)));
   FP8Q_DISPATCH(quant_1x128_kernel, bf16, mode, grid, st, rows, cols, ld_x, q, ld_q, scales);
   return hipGetLastError();
 }
