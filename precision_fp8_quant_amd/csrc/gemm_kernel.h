@@ -114,7 +114,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   constexpr int A_DMA = A_BYTES / 1024 / NW;     // 1 KB wave-wide DMA instructions per wave per stage
   constexpr int B_DMA = B_BYTES / 1024 / NW;
   static_assert(A_DMA * 1024 * NW == A_BYTES && B_DMA * 1024 * NW == B_BYTES, "DMA split");
-  static_assert(BN <= 256, "row scales: one DMA of at most 64 lanes x 4 floats");
+  static_assert(BSCALE != kScaleRow || BN <= 256, "row scales: one DMA of at most 64 lanes x 4 floats");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + SB_SLOTS * SB_BYTES];
   uint8_t* const sb_ring = smem + 2 * STAGE;
@@ -393,14 +393,20 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
 
 // Tile configurations, largest that divides the problem:
 //   256x256, 8 waves (4 along M x 2 along N) of 64x128
-//   128x256, 8 waves (2x4) of 64x64 for grouped GEMMs (one group per 128-row tile)
+//   grouped GEMMs (one group per 128-row tile): 128x512, 8 waves (2x4) of
+//   64x128 -- the same wave tile as 256x256, with both stages filling the
+//   160 KB of LDS (measured 7% faster than 128x256 on the MoE layer); else
+//   128x256, 8 waves (2x4) of 64x64
 //   128x256, 4 waves (2x2) of 64x128
 //   256x128, 4 waves (4x1) of 64x128
 //   128x128, 4 waves (2x2) of 64x64
 template <int BSCALE, int OUT, bool GROUPED, bool HW>
 static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   if (!GROUPED && a.M % 256 == 0 && a.N % 256 == 0) return launch_cfg<256, 256, 4, 2, BSCALE, OUT, GROUPED, HW>(a, st);
-  if (GROUPED && a.N % 256 == 0) return launch_cfg<128, 256, 2, 4, BSCALE, OUT, GROUPED, HW>(a, st);
+  if constexpr (GROUPED) {
+    if (a.N % 512 == 0) return launch_cfg<128, 512, 2, 4, BSCALE, OUT, GROUPED, HW>(a, st);
+    if (a.N % 256 == 0) return launch_cfg<128, 256, 2, 4, BSCALE, OUT, GROUPED, HW>(a, st);
+  }
   if (a.N % 256 == 0) return launch_cfg<128, 256, 2, 2, BSCALE, OUT, GROUPED, HW>(a, st);
   if (!GROUPED && a.M % 256 == 0) return launch_cfg<256, 128, 4, 1, BSCALE, OUT, GROUPED, HW>(a, st);
   return launch_cfg<128, 128, 2, 2, BSCALE, OUT, GROUPED, HW>(a, st);

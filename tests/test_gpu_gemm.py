@@ -126,10 +126,11 @@ def test_tiny_fprop_end_to_end():
     assert og.rel_frobenius(host(c), og.round_output(ref, "f32")) <= TOL_F32
 
 
-def test_grouped_small():
+@pytest.mark.parametrize("n", [256, 512])          # both grouped tile widths
+def test_grouped_small(n):
     fp8q = require_gpu()
     rng = np.random.default_rng(71)
-    g, n, k = 3, 256, 384
+    g, k = 3, 384
     gmap = np.array([0, 0, 2, 1, 2], dtype=np.int32)
     ops = random_fp8_operands(72, 128 * gmap.size, n * g, k)
     qa, sa = ops["qa"], ops["sa"]
