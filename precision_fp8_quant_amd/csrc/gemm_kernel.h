@@ -412,12 +412,41 @@ static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   return launch_cfg<128, 128, 2, 2, BSCALE, OUT, GROUPED, HW>(a, st);
 }
 
+// Balance the last wave of tiles (256 CUs): a 256x256 grid whose last wave
+// is at most half full leaves half the chip idle for a whole tile time.  When
+// those tail tiles form whole 256-column bands (block-scaled B only), the bands
+// run as a second grid of 128x256 tiles -- two per 256x256 tile, one full
+// wave -- right behind the first (e.g. Dgrad 8192x7168: 768 + 256 tiles
+// instead of 896 in 3.5 waves).
+template <int BSCALE, int OUT, bool GROUPED, bool HW>
+static hipError_t launch_balanced(const GemmArgs& a, hipStream_t st) {
+  constexpr int64_t kCUs = 256;
+  if constexpr (BSCALE == kScaleBlock && !GROUPED) {
+    if (a.M % 256 == 0 && a.N % 256 == 0) {
+      const int64_t tm = a.M / 256, tiles = tm * (a.N / 256);
+      const int64_t tail = tiles % kCUs;
+      if (tiles > kCUs && tail != 0 && 2 * tail <= kCUs && tail % tm == 0) {
+        GemmArgs head = a, rest = a;
+        rest.N = (tail / tm) * 256;
+        head.N = a.N - rest.N;
+        rest.b = a.b + head.N * a.ldb;
+        rest.sb = a.sb + (head.N / 128) * (a.K / 128);
+        rest.c = static_cast<uint8_t*>(a.c) + head.N * (OUT == kOutBF16 ? 2 : 4);
+        const hipError_t e = launch_cfg<256, 256, 4, 2, BSCALE, OUT, false, HW>(head, st);
+        if (e != hipSuccess) return e;
+        return launch_cfg<128, 256, 2, 4, BSCALE, OUT, false, HW>(rest, st);
+      }
+    }
+  }
+  return launch_tiles<BSCALE, OUT, GROUPED, HW>(a, st);
+}
+
 template <int BSCALE, bool GROUPED, bool HW>
 static hipError_t launch_out(const GemmArgs& a, int out, hipStream_t st) {
   switch (out) {
-    case kOutBF16: return launch_tiles<BSCALE, kOutBF16, GROUPED, HW>(a, st);
-    case kOutF32: return launch_tiles<BSCALE, kOutF32, GROUPED, HW>(a, st);
-    default: return launch_tiles<BSCALE, kOutF32Acc, GROUPED, HW>(a, st);
+    case kOutBF16: return launch_balanced<BSCALE, kOutBF16, GROUPED, HW>(a, st);
+    case kOutF32: return launch_balanced<BSCALE, kOutF32, GROUPED, HW>(a, st);
+    default: return launch_balanced<BSCALE, kOutF32Acc, GROUPED, HW>(a, st);
   }
 }
 

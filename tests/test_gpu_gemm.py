@@ -77,6 +77,28 @@ def test_random_operands(kind, out, mnk):
         assert err <= TOL_F32, err
 
 
+@pytest.mark.parametrize("kind", ["fprop", "dgrad"])
+@pytest.mark.parametrize("out", ["bf16", "f32acc"])
+def test_tail_balanced_two_grid_launch(kind, out):
+    """M=512, N=129*256: 258 tiles of 256x256 on 256 CUs, so the last 256-column
+    band runs as a second grid of 128x256 tiles; every output is checked."""
+    fp8q = require_gpu()
+    m, n, k = 512, 129 * 256, 256
+    ops = random_fp8_operands(201, m, n, k, kind=kind)
+    ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind)
+    args = [dev(ops[x]) for x in ("qa", "sa", "qb", "sb")]
+    if out == "bf16":
+        c = fp8q.fp8_gemm_blockscaled(KINDS[kind], *args, out_dtype=torch.bfloat16)
+        got, want, tol = host_bf16_as_f64(c), og.round_bf16(ref), TOL
+    else:
+        c0 = np.random.default_rng(202).standard_normal((m, n)).astype(np.float32)
+        c = dev(c0.copy())
+        fp8q.fp8_gemm_blockscaled(KINDS[kind], *args, c=c, accumulate=True)
+        got, want, tol = host(c).astype(np.float64), ref + c0.astype(np.float64), TOL_F32
+    for cols in (slice(0, 128 * 256), slice(128 * 256, n)):          # first grid, second grid
+        assert og.rel_frobenius(got[:, cols], want[:, cols]) <= tol, cols
+
+
 def test_wgrad_accumulate_into_fp32():
     fp8q = require_gpu()
     m, n, k = 256, 256, 512
