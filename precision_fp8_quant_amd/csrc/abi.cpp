@@ -31,6 +31,40 @@ bool dtype_ok(int dt) { return dt == FP8Q_BF16 || dt == FP8Q_F32; }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_HIP; }
 
+// Shared validation of the two plain GEMM entry points; on success the
+// caller launches.
+int check_gemm(int kind, int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                      const float* a_scales, const uint8_t* b, int64_t ldb, const float* b_scales, void* c,
+                      int c_dtype, int64_t ldc, int accumulate, bool* nothing_to_do) {
+  *nothing_to_do = false;
+  if (kind != FP8Q_FPROP && kind != FP8Q_DGRAD && kind != FP8Q_WGRAD) return FP8Q_ERR_ARG;
+  if (!dtype_ok(c_dtype) || (accumulate != 0 && accumulate != 1)) return FP8Q_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
+  if (M == 0 || N == 0) {
+    *nothing_to_do = true;
+    return FP8Q_OK;
+  }
+  if (!c) return FP8Q_ERR_NULL;
+  if (K > 0 && (!a || !b || !a_scales || !b_scales)) return FP8Q_ERR_NULL;
+  if (ldc < N || (K > 0 && (lda < K || ldb < K))) return FP8Q_ERR_SHAPE;
+  const int64_t es = dtype_size(c_dtype);
+  if (!aligned16(c) || (ldc * es) % 16) return FP8Q_ERR_ALIGN;
+  if (K > 0 && (!aligned16(a) || !aligned16(b) || !aligned16(a_scales) || !aligned16(b_scales) ||
+                lda % 16 || ldb % 16))
+    return FP8Q_ERR_ALIGN;
+  if (M % 128 || N % 128 || K % 128) return FP8Q_ERR_UNSUPPORTED;
+  if (accumulate && c_dtype != FP8Q_F32) return FP8Q_ERR_UNSUPPORTED;
+  if ((M / 128) * (N / 128) > kMaxGridX) return FP8Q_ERR_UNSUPPORTED;
+  const int64_t nsa = (K / 128) * M;
+  const int64_t nsb = kind == FP8Q_WGRAD ? (K / 128) * N : (N / 128) * (K / 128);
+  const Range rc = span(c, M, N, ldc, es);
+  const Range ins[4] = {span(a, M, K, lda, 1), span(b, N, K, ldb, 1),
+                        span(a_scales, 1, nsa, nsa, 4), span(b_scales, 1, nsb, nsb, 4)};
+  for (int i = 0; i < 4; ++i)
+    if (overlap(rc, ins[i])) return FP8Q_ERR_ALIAS;
+  return FP8Q_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,40 +171,6 @@ int fp8_requant_1x128_to_128x1(const uint8_t* q, int64_t rows, int64_t cols, int
       if (overlap(ins[i], outs[j])) return FP8Q_ERR_ALIAS;
   return from_hip(fp8q::launch_requant_128x1(q, rows, cols, ld_q, scales, mode, q_t, ld_qt, scales_t,
                                              reinterpret_cast<hipStream_t>(stream)));
-}
-
-// Shared validation of the two plain GEMM entry points; on success the
-// caller launches.
-static int check_gemm(int kind, int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
-                      const float* a_scales, const uint8_t* b, int64_t ldb, const float* b_scales, void* c,
-                      int c_dtype, int64_t ldc, int accumulate, bool* nothing_to_do) {
-  *nothing_to_do = false;
-  if (kind != FP8Q_FPROP && kind != FP8Q_DGRAD && kind != FP8Q_WGRAD) return FP8Q_ERR_ARG;
-  if (!dtype_ok(c_dtype) || (accumulate != 0 && accumulate != 1)) return FP8Q_ERR_ARG;
-  if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
-  if (M == 0 || N == 0) {
-    *nothing_to_do = true;
-    return FP8Q_OK;
-  }
-  if (!c) return FP8Q_ERR_NULL;
-  if (K > 0 && (!a || !b || !a_scales || !b_scales)) return FP8Q_ERR_NULL;
-  if (ldc < N || (K > 0 && (lda < K || ldb < K))) return FP8Q_ERR_SHAPE;
-  const int64_t es = dtype_size(c_dtype);
-  if (!aligned16(c) || (ldc * es) % 16) return FP8Q_ERR_ALIGN;
-  if (K > 0 && (!aligned16(a) || !aligned16(b) || !aligned16(a_scales) || !aligned16(b_scales) ||
-                lda % 16 || ldb % 16))
-    return FP8Q_ERR_ALIGN;
-  if (M % 128 || N % 128 || K % 128) return FP8Q_ERR_UNSUPPORTED;
-  if (accumulate && c_dtype != FP8Q_F32) return FP8Q_ERR_UNSUPPORTED;
-  if ((M / 128) * (N / 128) > kMaxGridX) return FP8Q_ERR_UNSUPPORTED;
-  const int64_t nsa = (K / 128) * M;
-  const int64_t nsb = kind == FP8Q_WGRAD ? (K / 128) * N : (N / 128) * (K / 128);
-  const Range rc = span(c, M, N, ldc, es);
-  const Range ins[4] = {span(a, M, K, lda, 1), span(b, N, K, ldb, 1),
-                        span(a_scales, 1, nsa, nsa, 4), span(b_scales, 1, nsb, nsb, 4)};
-  for (int i = 0; i < 4; ++i)
-    if (overlap(rc, ins[i])) return FP8Q_ERR_ALIAS;
-  return FP8Q_OK;
 }
 
 int fp8_gemm_blockscaled(int kind, int64_t M, int64_t N, int64_t K,
