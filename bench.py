@@ -163,6 +163,10 @@ class Step:
             ("gemm Wgrad pow2 (hardware-scaled MFMA)", lambda: q.fp8_gemm_blockscaled_pow2(
                 q.WGRAD, self.qdyt_p2, self.sdyt_p2, self.rq_qt, self.rq_st, c=self.dw),
              gf(D_OUT, D_IN, T), "flop"),
+            # max-abs dY^T (from the step) against the power-of-two X^T: only B's scales in the MFMA
+            ("gemm Wgrad, pow2 X only (B scales in the MFMA)", lambda: q.fp8_gemm_blockscaled_pow2(
+                q.WGRAD, self.qdyt, self.sdyt, self.rq_qt, self.rq_st, c=self.dw, pow2_operands=q.POW2_B),
+             gf(D_OUT, D_IN, T), "flop"),
         ]
         self.step_flop = sum(w for _, _, w, kind in self.kernels if kind == "flop")
 

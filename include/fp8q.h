@@ -72,6 +72,7 @@ typedef enum { FP8Q_BF16 = 0, FP8Q_F32 = 1 } fp8q_dtype;
 typedef enum { FP8Q_SCALE_MAXABS = 0, FP8Q_SCALE_POW2 = 1 } fp8q_scale_mode;
 typedef enum { FP8Q_TILE_1x128 = 0, FP8Q_TILE_128x1 = 1 } fp8q_tile;
 typedef enum { FP8Q_FPROP = 0, FP8Q_DGRAD = 1, FP8Q_WGRAD = 2 } fp8q_gemm_kind;
+typedef enum { FP8Q_POW2_A = 1, FP8Q_POW2_B = 2, FP8Q_POW2_AB = 3 } fp8q_pow2_operands;
 
 /*
  * fp8_quant_tile -- online 1x128 or 128x1 tile quantization.
@@ -151,25 +152,34 @@ int fp8_gemm_blockscaled(int kind, int64_t M, int64_t N, int64_t K,
                          void* stream);
 
 /*
- * fp8_gemm_blockscaled_pow2 -- the same GEMM for operands whose scales are
- * all integral powers of two (FP8Q_SCALE_POW2 quantizer output), with the
- * group scaling done by the matrix cores themselves.
+ * fp8_gemm_blockscaled_pow2 -- the same GEMM when one or both operands carry
+ * power-of-two scales (FP8Q_SCALE_POW2 quantizer output), with those scales
+ * applied by the matrix cores themselves.
  * [dssusan.co.kr FP8 excerpt, paragraph 1: power-of-2 scales; paragraph 3 and
  *  "Deepseek - Not For everyone", paragraph 4: MMA with group scaling]
  *
- * Arguments, layouts, shape rules and status codes are exactly those of
- * fp8_gemm_blockscaled.  Each scale is handed to gfx950's
- * v_mfma_scale_f32_16x16x128_f8f6f4 as an E8M0 code (its biased exponent), so
- * every 128-deep group is dequantized inside the MFMA and accumulated in the
- * MFMA's own FP32 accumulator across all K-groups: there is no per-group VALU
- * promotion.  Only the exponent field of each scale is used: a scale that is
- * not a positive power of two in [2^-126, 2^127] gives unspecified output.
+ * Arguments, layouts, shape rules and status codes are those of
+ * fp8_gemm_blockscaled, plus
+ * pow2_operands : FP8Q_POW2_A, FP8Q_POW2_B or FP8Q_POW2_AB -- whose scales are
+ *                 powers of two (anything else: FP8Q_ERR_ARG).
+ * Each power-of-two scale is handed to gfx950's
+ * v_mfma_scale_f32_16x16x128_f8f6f4 as an E8M0 code (its biased exponent),
+ * so that operand is dequantized inside the MFMA:
+ *   FP8Q_POW2_AB: every 128-deep group is dequantized and accumulated in the
+ *                 MFMA's own FP32 accumulator across all K-groups; there is no
+ *                 per-group VALU promotion at all;
+ *   FP8Q_POW2_A / FP8Q_POW2_B: the other operand's scale is applied by the
+ *                 per-group FP32 promotion as in fp8_gemm_blockscaled (for
+ *                 Wgrad this saves one multiply per output element per group).
+ * Only the exponent field of a scale declared power-of-two is used: such a
+ * scale that is not a positive power of two in [2^-126, 2^127] gives
+ * unspecified output.
  */
 int fp8_gemm_blockscaled_pow2(int kind, int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, int64_t lda, const float* a_scales,
                               const uint8_t* b, int64_t ldb, const float* b_scales,
                               void* c, int c_dtype, int64_t ldc, int accumulate,
-                              void* stream);
+                              int pow2_operands, void* stream);
 
 /*
  * fp8_gemm_blockscaled_grouped -- grouped (MoE expert) Fprop.

@@ -10,7 +10,7 @@ Functions keep the C names:
     fp8_quant_tile(x, tile, mode)              -> (q, scales)
     fp8_quant_block(w, mode, transposed)       -> (q, scales[, q_t, scales_t])
     fp8_gemm_blockscaled(kind, a, sa, b, sb)   -> c
-    fp8_gemm_blockscaled_pow2(kind, a, sa, b, sb)   -> c   (power-of-two scales)
+    fp8_gemm_blockscaled_pow2(kind, a, sa, b, sb, pow2_operands) -> c   (power-of-two scales)
     fp8_gemm_blockscaled_grouped(gmap, a, sa, b, sb) -> c
     fp8_requant_1x128_to_128x1(q, scales, mode) -> (q_t, scales_t)
 FP8 tensors are torch.uint8 holding OCP E4M3FN codes.
@@ -30,6 +30,7 @@ BF16, F32 = 0, 1
 MAXABS, POW2 = 0, 1
 TILE_1x128, TILE_128x1 = 0, 1
 FPROP, DGRAD, WGRAD = 0, 1, 2
+POW2_A, POW2_B, POW2_AB = 1, 2, 3
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -43,7 +44,7 @@ SIGNATURES = {
     "fp8_gemm_blockscaled": [_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _int, _i64,
                              _int, _ptr],
     "fp8_gemm_blockscaled_pow2": [_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _int, _i64,
-                                  _int, _ptr],
+                                  _int, _int, _ptr],
     "fp8_gemm_blockscaled_grouped": [_i32, _i64, _i64, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _int,
                                      _i64, _ptr],
     "fp8_requant_1x128_to_128x1": [_ptr, _i64, _i64, _i64, _ptr, _int, _ptr, _i64, _ptr, _ptr],
@@ -171,12 +172,14 @@ def fp8_gemm_blockscaled(kind, a, a_scales, b, b_scales, out_dtype=torch.bfloat1
 
 
 def fp8_gemm_blockscaled_pow2(kind, a, a_scales, b, b_scales, out_dtype=torch.bfloat16, c=None,
-                              accumulate=False, stream=None):
-    """Same GEMM for power-of-two scales, applied by the hardware-scaled MFMA."""
-    return _gemm(lib.fp8_gemm_blockscaled_pow2, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream)
+                              accumulate=False, pow2_operands=POW2_AB, stream=None):
+    """Same GEMM with the power-of-two scales of A, B or both (pow2_operands)
+    applied by the hardware-scaled MFMA."""
+    return _gemm(lib.fp8_gemm_blockscaled_pow2, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream,
+                 extra=(int(pow2_operands),))
 
 
-def _gemm(fn, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream):
+def _gemm(fn, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream, extra=()):
     a, b = _codes(_rowmajor(a, "a")), _codes(_rowmajor(b, "b"))
     m, k = a.shape
     n = b.shape[0]
@@ -186,7 +189,7 @@ def _gemm(fn, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream):
         c = torch.empty((m, n), dtype=out_dtype, device=a.device)
     _rowmajor(c, "c")
     _check(fn(kind, m, n, k, a.data_ptr(), _ld(a), a_scales.data_ptr(), b.data_ptr(), _ld(b), b_scales.data_ptr(),
-              c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0, _stream(stream)))
+              c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0, *extra, _stream(stream)))
     return c
 
 

@@ -69,7 +69,7 @@ int check_gemm(int kind, int64_t M, int64_t N, int64_t K, const uint8_t* a, int6
 
 extern "C" {
 
-int fp8q_abi_version(void) { return 102; }
+int fp8q_abi_version(void) { return 103; }
 
 const char* fp8q_status_string(int s) {
   switch (s) {
@@ -189,14 +189,20 @@ int fp8_gemm_blockscaled(int kind, int64_t M, int64_t N, int64_t K,
 int fp8_gemm_blockscaled_pow2(int kind, int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, int64_t lda, const float* a_scales,
                               const uint8_t* b, int64_t ldb, const float* b_scales,
-                              void* c, int c_dtype, int64_t ldc, int accumulate, void* stream) {
+                              void* c, int c_dtype, int64_t ldc, int accumulate, int pow2_operands,
+                              void* stream) {
+  if (pow2_operands != FP8Q_POW2_A && pow2_operands != FP8Q_POW2_B && pow2_operands != FP8Q_POW2_AB)
+    return FP8Q_ERR_ARG;
   bool nothing = false;
   const int st = check_gemm(kind, M, N, K, a, lda, a_scales, b, ldb, b_scales, c, c_dtype, ldc, accumulate,
                             &nothing);
   if (st != FP8Q_OK || nothing) return st;
-  return from_hip(fp8q::launch_gemm_pow2(kind, M, N, K, a, lda, a_scales, b, ldb, b_scales, c,
-                                         c_dtype == FP8Q_BF16, ldc, accumulate != 0,
-                                         reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (pow2_operands == FP8Q_POW2_AB)
+    return from_hip(fp8q::launch_gemm_pow2(kind, M, N, K, a, lda, a_scales, b, ldb, b_scales, c,
+                                           c_dtype == FP8Q_BF16, ldc, accumulate != 0, s));
+  return from_hip(fp8q::launch_gemm_pow2_one(kind, pow2_operands, M, N, K, a, lda, a_scales, b, ldb, b_scales,
+                                             c, c_dtype == FP8Q_BF16, ldc, accumulate != 0, s));
 }
 
 int fp8_gemm_blockscaled_grouped(int32_t num_groups, int64_t M_total, int64_t N, int64_t K,

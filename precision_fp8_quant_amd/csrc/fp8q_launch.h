@@ -27,11 +27,17 @@ hipError_t launch_gemm(int kind, int64_t M, int64_t N, int64_t K,
                        const uint8_t* b, int64_t ldb, const float* sb,
                        void* c, bool out_bf16, int64_t ldc, bool accumulate, hipStream_t st);
 
-// Same operands; power-of-two scales applied by the hardware-scaled MFMA.
+// Same operands; both operands' power-of-two scales applied by the hardware-scaled MFMA.
 hipError_t launch_gemm_pow2(int kind, int64_t M, int64_t N, int64_t K,
                             const uint8_t* a, int64_t lda, const float* sa,
                             const uint8_t* b, int64_t ldb, const float* sb,
                             void* c, bool out_bf16, int64_t ldc, bool accumulate, hipStream_t st);
+
+// One operand power-of-two (1: A, 2: B) applied by the MFMA, the other promoted.
+hipError_t launch_gemm_pow2_one(int kind, int pow2_operands, int64_t M, int64_t N, int64_t K,
+                                const uint8_t* a, int64_t lda, const float* sa,
+                                const uint8_t* b, int64_t ldb, const float* sb,
+                                void* c, bool out_bf16, int64_t ldc, bool accumulate, hipStream_t st);
 
 hipError_t launch_gemm_grouped(int32_t num_groups, int64_t M_total, int64_t N, int64_t K,
                                const int32_t* group_of_mtile,

@@ -26,10 +26,13 @@
 // XOR-swizzled by row) -> ds_read_b128 fragments -> MFMA -> FMA into FP32
 // accumulators.
 //
-// The same template with HW=true is the hardware-scaled variant for
-// power-of-two scales: v_mfma_scale_f32_16x16x128_f8f6f4 receives the A-row
-// and B-row/block scales as E8M0 exponents and accumulates every group in
-// place, so the loop carries no VALU work (instantiated in gemm_pow2.hip).
+// The template parameter HW says which operands' scales are powers of two
+// and applied by the matrix core itself (v_mfma_scale_f32_16x16x128_f8f6f4
+// takes them as E8M0 exponents): kHwNone, kHwA, kHwB, or kHwAB.  With both,
+// every group accumulates in place in the MFMA and the loop carries no VALU
+// work (instantiated in gemm_pow2.hip); with one, the other operand's scale
+// is the only factor left for the promotion FMA, which for Wgrad saves the
+// per-element multiply.
 #pragma once
 
 #include "fp8q_launch.h"
@@ -45,6 +48,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 enum { kScaleBlock = 0, kScaleRow = 1 };   // B scales: 128x128 blocks, or per-row (128x1 tiles)
 enum { kOutBF16 = 0, kOutF32 = 1, kOutF32Acc = 2 };
+enum { kHwNone = 0, kHwA = 1, kHwB = 2, kHwAB = 3 };   // power-of-two scales applied in the MFMA
 
 struct GemmArgs {
   const uint8_t* a; int64_t lda; const float* sa;
@@ -97,7 +101,7 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lq) {
   return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
 }
 
-template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, bool HW>
+template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, int HW>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM;          // wave tile rows (M)
@@ -194,8 +198,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   const int64_t n_wave = n0 + wn * TN;                      // + 64*pn + 16*lq + 4*js + j
 
   // Promoted path: FP32 accumulators updated by VALU FMAs once per group.
-  // Hardware-scaled path (HW): the MFMA applies both power-of-two scales
-  // itself and accumulates every group into accv (no VALU work at all).
+  // Both scales in hardware (kHwAB): the MFMA applies both power-of-two
+  // scales itself and accumulates every group into accv (no VALU work).
+  constexpr bool IN_MFMA = HW == kHwAB;           // accumulate inside the MFMA
+  constexpr bool A_HW = (HW & kHwA) != 0;         // A-row scale applied by the MFMA
+  constexpr bool B_HW = (HW & kHwB) != 0;         // B-row / block scale applied by the MFMA
   float acc[SM][PN][4][4];
   v4f accv[SM][PN][4];
 #pragma unroll
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     for (int b = 0; b < PN; ++b)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if constexpr (HW) accv[a][b][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (IN_MFMA) accv[a][b][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) acc[a][b][c][d] = 0.0f;
       }
@@ -215,8 +222,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   // fragment bi = t/SM against A fragment ms = t%SM):
   //  * promoted path: MFMA t writes result slot t%3 and the promotion FMAs of
   //    MFMA t-2 follow it, so a VALU op never waits on the MFMA just issued;
-  //  * hardware-scaled path (HW): the MFMA takes both E8M0 scales and
-  //    accumulates in place; nothing else runs;
+  //  * kHwAB: the MFMA takes both E8M0 scales and accumulates in place;
+  //    nothing else runs (kHwA / kHwB: the MFMA takes one scale, the FMA the
+  //    other);
   //  * fragment reads run ahead of their MFMAs: the group's A fragments and B
   //    fragments 0-1 up front, then B fragment bi+2 (with the per-column
   //    Wgrad scales it needs) right after the first MFMA of block bi.  The
@@ -228,12 +236,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   // hazard with s_nop).
   constexpr int NB = PN * 4;            // B fragments per group
   constexpr int NT = NB * SM;           // MFMAs per group
-  constexpr int LAG = HW ? 0 : 2;
-  static_assert(!(HW && GROUPED), "the hardware-scaled path covers the plain GEMMs");
+  constexpr int LAG = IN_MFMA ? 0 : 2;
+  static_assert(HW == kHwNone || !GROUPED, "the hardware-scaled paths cover the plain GEMMs");
 
   auto frag_row_b = [&](int bi) { return wn * TN + 16 * bi + lr; };
   auto sbq_off = [&](int bi) { return (wn * TN + 64 * (bi >> 2) + 16 * lq + 4 * (bi & 3)) * 4; };
-  // HW: the source-A row this lane feeds in B fragment bi is the LDS row
+  // B_HW: the source-A row this lane feeds in B fragment bi is the LDS row
   // frag_row_b(bi), i.e. tile column wn*TN + 64*(bi/4) + 16*(lr/4) + 4*(bi%4) + lr%4.
   // A power-of-two float's E8M0 code is its biased exponent field.
   auto sbe_read = [&](const uint8_t* ring, int bi) {
@@ -268,25 +276,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     const uint8_t* ta = smem + stage * STAGE;
     const uint8_t* tb = ta + A_BYTES;
     const uint8_t* ts = sb_ring + stage * SB_BYTES;
+    // cs: the promotion factor of A fragment ms (everything the MFMA does not
+    // apply, except Wgrad's per-column B scale, which sbq carries)
     float cs[SM];
-    uint32_t sae[SM];                                   // HW: E8M0 codes of the A-row scales
+    uint32_t sae[SM];                                   // A_HW: E8M0 codes of the A-row scales
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) {
-      cs[ms] = BSCALE == kScaleBlock ? sa_cur[ms] * sb_cur : sa_cur[ms];
-      sae[ms] = __float_as_uint(sa_cur[ms]) >> 23;
+      const float fa = A_HW ? 1.0f : sa_cur[ms];
+      cs[ms] = (BSCALE == kScaleBlock && !B_HW) ? fa * sb_cur : fa;
+      sae[ms] = A_HW ? __float_as_uint(sa_cur[ms]) >> 23 : 127u;   // 127: E8M0 code of 1.0
     }
     const uint32_t sbe_blk = __float_as_uint(sb_cur) >> 23;
 
     v8i af[SM];
     v8i bfb[3];
-    v4f sbq[3];                             // promoted Wgrad: slot b%3 holds block b's column scales
-    uint32_t sbe[3];                        // HW Wgrad: slot b%3 holds this lane's B-row E8M0 code
+    v4f sbq[3];                             // Wgrad, B promoted: slot b%3 holds block b's column scales
+    uint32_t sbe[3];                        // Wgrad, B in the MFMA: slot b%3 holds this lane's B-row code
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) af[ms] = read_frag(ta, wm * TM + 16 * ms + lr, lq);
     bfb[0] = read_frag(tb, frag_row_b(0), lq);
     if (NB > 1) bfb[1] = read_frag(tb, frag_row_b(1), lq);
     if constexpr (BSCALE == kScaleRow) {
-      if constexpr (HW) {
+      if constexpr (B_HW) {
         sbe[0] = sbe_read(ts, 0);
         if (NB > 1) sbe[1] = sbe_read(ts, 1);
       } else {
@@ -298,13 +309,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     for (int t = 0; t < NT + LAG; ++t) {
       if (t < NT) {
         const int bi = t / SM, ms = t % SM;
-        if constexpr (HW) {
+        if constexpr (IN_MFMA) {
           // v_mfma_scale_f32_16x16x128_f8f6f4: E8M0 scale of source A (this
           // lane's B row) and of source B (this lane's A row) applied in the
           // matrix core, result accumulated in place
           const uint32_t sb_e = BSCALE == kScaleRow ? sbe[bi % 3] : sbe_blk;
           accv[ms][bi >> 2][bi & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               bfb[bi % 3], af[ms], accv[ms][bi >> 2][bi & 3], 0, 0, 0, sb_e, 0, sae[ms]);
+        } else if constexpr (HW != kHwNone) {
+          // one operand's scale in the matrix core (the other's is 2^0), the
+          // partial then promoted like below
+          const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+          const uint32_t sb_e = !B_HW ? 127u : (BSCALE == kScaleRow ? sbe[bi % 3] : sbe_blk);
+          dq[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfb[bi % 3], af[ms], zero, 0, 0, 0, sb_e, 0,
+                                                                      sae[ms]);
         } else {
           const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
           dq[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfb[bi % 3], af[ms], zero, 0, 0, 0, 0, 0, 0);
@@ -312,22 +330,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
         if (ms == 0) {
           if (bi + 2 < NB) {
             bfb[(bi + 2) % 3] = read_frag(tb, frag_row_b(bi + 2), lq);
-            if constexpr (HW && BSCALE == kScaleRow) sbe[(bi + 2) % 3] = sbe_read(ts, bi + 2);
+            if constexpr (B_HW && BSCALE == kScaleRow) sbe[(bi + 2) % 3] = sbe_read(ts, bi + 2);
           }
-          if constexpr (!HW && BSCALE == kScaleRow)
+          if constexpr (!B_HW && BSCALE == kScaleRow)
             if (bi + 1 < NB) sbq[(bi + 1) % 3] = *reinterpret_cast<const v4f*>(ts + sbq_off(bi + 1));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (!HW && t >= LAG) {
+      if (!IN_MFMA && t >= LAG) {
         const int u = t - LAG;
         const int bu = u / SM, mu = u % SM;
         const int pn = bu >> 2, js = bu & 3;
         const v4f d = dq[u % 3];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float dj = BSCALE == kScaleRow ? d[j] * sbq[bu % 3][j] : d[j];
-          acc[mu][pn][js][j] = __builtin_fmaf(dj, cs[mu], acc[mu][pn][js][j]);
+          if constexpr (BSCALE == kScaleRow && !B_HW && A_HW) {
+            acc[mu][pn][js][j] = __builtin_fmaf(d[j], sbq[bu % 3][j], acc[mu][pn][js][j]);
+          } else {
+            const float dj = (BSCALE == kScaleRow && !B_HW) ? d[j] * sbq[bu % 3][j] : d[j];
+            acc[mu][pn][js][j] = __builtin_fmaf(dj, cs[mu], acc[mu][pn][js][j]);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // keep step t's MFMA and step t-2's FMAs together
@@ -338,7 +360,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     wait_vmem_all();
     __syncthreads();
   }
-  if constexpr (HW) {
+  if constexpr (IN_MFMA) {
 #pragma unroll
     for (int a = 0; a < SM; ++a)
 #pragma unroll
@@ -382,7 +404,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
 // ---------------------------------------------------------------------------
 // Launch configurations.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, bool HW>
+template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, int HW>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles = (a.M / BM) * (a.N / BN);
   if (tiles == 0) return hipSuccess;
@@ -400,7 +422,7 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
 //   128x256, 4 waves (2x2) of 64x128
 //   256x128, 4 waves (4x1) of 64x128
 //   128x128, 4 waves (2x2) of 64x64
-template <int BSCALE, int OUT, bool GROUPED, bool HW>
+template <int BSCALE, int OUT, bool GROUPED, int HW>
 static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   if (!GROUPED && a.M % 256 == 0 && a.N % 256 == 0) return launch_cfg<256, 256, 4, 2, BSCALE, OUT, GROUPED, HW>(a, st);
   if constexpr (GROUPED) {
@@ -418,7 +440,7 @@ static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
 // run as a second grid of 128x256 tiles -- two per 256x256 tile, one full
 // wave -- right behind the first (e.g. Dgrad 8192x7168: 768 + 256 tiles
 // instead of 896 in 3.5 waves).
-template <int BSCALE, int OUT, bool GROUPED, bool HW>
+template <int BSCALE, int OUT, bool GROUPED, int HW>
 static hipError_t launch_balanced(const GemmArgs& a, hipStream_t st) {
   constexpr int64_t kCUs = 256;
   if constexpr (BSCALE == kScaleBlock && !GROUPED) {
@@ -441,7 +463,7 @@ static hipError_t launch_balanced(const GemmArgs& a, hipStream_t st) {
   return launch_tiles<BSCALE, OUT, GROUPED, HW>(a, st);
 }
 
-template <int BSCALE, bool GROUPED, bool HW>
+template <int BSCALE, bool GROUPED, int HW>
 static hipError_t launch_out(const GemmArgs& a, int out, hipStream_t st) {
   switch (out) {
     case kOutBF16: return launch_balanced<BSCALE, kOutBF16, GROUPED, HW>(a, st);

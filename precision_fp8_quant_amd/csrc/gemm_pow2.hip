@@ -18,8 +18,8 @@ hipError_t launch_gemm_pow2(int kind, int64_t M, int64_t N, int64_t K,
                             void* c, bool out_bf16, int64_t ldc, bool accumulate, hipStream_t st) {
   GemmArgs args{a, lda, sa, b, ldb, sb, c, ldc, M, N, K, nullptr, 0, 0, 0};
   const int out = out_bf16 ? kOutBF16 : (accumulate ? kOutF32Acc : kOutF32);
-  if (kind == 2) return launch_out<kScaleRow, false, true>(args, out, st);
-  return launch_out<kScaleBlock, false, true>(args, out, st);
+  if (kind == 2) return launch_out<kScaleRow, false, kHwAB>(args, out, st);
+  return launch_out<kScaleBlock, false, kHwAB>(args, out, st);
 }
 
 }  // namespace fp8q

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert fp8q.lib.fp8q_abi_version() == 102
+    assert fp8q.lib.fp8q_abi_version() == 103
     for s in range(8):
         assert fp8q.status_string(s).startswith("FP8Q_")
     assert fp8q.status_string(99) == "unknown fp8q status"
@@ -92,11 +92,12 @@ def test_quant_block_validation():
 
 def _gemm(fn="fp8_gemm_blockscaled", **kw):
     args = dict(kind=fp8q.FPROP, M=256, N=256, K=512, a=A, lda=512, sa=B, b=C, ldb=512, sb=D,
-                c=0x7000000, cdt=fp8q.BF16, ldc=256, acc=0)
+                c=0x7000000, cdt=fp8q.BF16, ldc=256, acc=0, pow2=fp8q.POW2_AB)
     args.update(kw)
+    extra = (args["pow2"],) if fn == "fp8_gemm_blockscaled_pow2" else ()
     return getattr(fp8q.lib, fn)(args["kind"], args["M"], args["N"], args["K"], args["a"], args["lda"],
-                                         args["sa"], args["b"], args["ldb"], args["sb"], args["c"], args["cdt"],
-                                         args["ldc"], args["acc"], None)
+                                 args["sa"], args["b"], args["ldb"], args["sb"], args["c"], args["cdt"],
+                                 args["ldc"], args["acc"], *extra, None)
 
 
 @pytest.mark.parametrize("fn", ["fp8_gemm_blockscaled", "fp8_gemm_blockscaled_pow2"])
@@ -114,6 +115,13 @@ def test_gemm_validation(fn):
     assert _gemm(fn, M=200) == fp8q.ERR_UNSUPPORTED
     assert _gemm(fn, acc=1) == fp8q.ERR_UNSUPPORTED              # accumulate needs FP32 output
     assert _gemm(fn, c=A + 4096) == fp8q.ERR_ALIAS
+
+
+def test_pow2_gemm_operand_mask_validation():
+    for bad in (0, 4, -1):
+        assert _gemm("fp8_gemm_blockscaled_pow2", pow2=bad) == fp8q.ERR_ARG
+    for ok in (fp8q.POW2_A, fp8q.POW2_B, fp8q.POW2_AB):
+        assert _gemm("fp8_gemm_blockscaled_pow2", pow2=ok, M=0) == fp8q.OK
 
 
 def _grouped(**kw):

@@ -20,7 +20,19 @@ from workloads import linear_layer, output_grad, random_fp8_operands
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3
+TOL_F32 = 2e-4      # same FP32-output bound as the promoted GEMM (8-product MFMA blocks)
 KINDS = {"fprop": 0, "dgrad": 1, "wgrad": 2}
+MASKS = {"A": 1, "B": 2, "AB": 3}
+
+
+def _mixed_operands(seed, m, n, k, kind, mask):
+    """Random codes; the scales of the operands named in mask are powers of two,
+    the others arbitrary positive floats."""
+    p2 = random_fp8_operands(seed, m, n, k, kind=kind, pow2=True)
+    anyv = random_fp8_operands(seed, m, n, k, kind=kind, pow2=False)
+    return {"qa": p2["qa"], "qb": p2["qb"],
+            "sa": p2["sa"] if "A" in mask else anyv["sa"],
+            "sb": p2["sb"] if "B" in mask else anyv["sb"]}
 
 
 def _out_host(c):
@@ -79,6 +91,44 @@ def test_pow2_extreme_scale_exponents():
         assert og.rel_frobenius(got[r], og.round_output(ref[r], "f32")) <= TOL, r
 
 
+@pytest.mark.parametrize("mask", ["A", "B"])
+@pytest.mark.parametrize("kind", ["fprop", "dgrad", "wgrad"])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("mnk", [(256, 384, 640), (384, 256, 1024), (512, 512, 2048)])
+def test_one_pow2_operand_random(mask, kind, out, mnk):
+    """One operand's scales applied in the MFMA, the other's by the promotion."""
+    fp8q = require_gpu()
+    m, n, k = mnk
+    ops = _mixed_operands(211 + m + n + k, m, n, k, kind, mask)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    c = fp8q.fp8_gemm_blockscaled_pow2(KINDS[kind], dev(ops["qa"]), dev(ops["sa"]), dev(ops["qb"]), dev(ops["sb"]),
+                                       out_dtype=dt, pow2_operands=MASKS[mask])
+    ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind)
+    err = og.rel_frobenius(_out_host(c), og.round_output(ref, out))
+    assert err <= (TOL if out == "bf16" else TOL_F32), err
+
+
+@pytest.mark.parametrize("mask", ["A", "B"])
+@pytest.mark.parametrize("kind", ["fprop", "wgrad"])
+def test_one_pow2_operand_exact_small_integers(mask, kind):
+    fp8q = require_gpu()
+    rng = np.random.default_rng(221)
+    m, n, k = 256, 256, 384
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50], np.uint8)
+    def codes(shape):
+        c = ints[rng.integers(0, ints.size, size=shape)]
+        return (c | (rng.integers(0, 2, size=shape) << 7).astype(np.uint8)).astype(np.uint8)
+    qa, qb = codes((m, k)), codes((n, k))
+    sa = np.exp2(rng.integers(-3, 3, size=(k // 128, m))).astype(np.float32)
+    shape_b = (k // 128, n) if kind == "wgrad" else (n // 128, k // 128)
+    sb = np.exp2(rng.integers(-2, 3, size=shape_b)).astype(np.float32)
+    c = fp8q.fp8_gemm_blockscaled_pow2(KINDS[kind], dev(qa), dev(sa), dev(qb), dev(sb), out_dtype=torch.float32,
+                                       pow2_operands=MASKS[mask])
+    ref = og.gemm_ref(qa, sa, qb, sb, kind, exact_int=True)
+    got = _out_host(c)
+    assert np.array_equal(got, ref), f"max abs diff {np.max(np.abs(got - ref))}"
+
+
 def test_pow2_wgrad_accumulate_and_k_zero():
     fp8q = require_gpu()
     m, n, k = 256, 512, 384
@@ -132,6 +182,26 @@ def test_pow2_fprop_full_size_sampled(layer):
     ref = og.gemm_ref_entries(qx_r, sx_r, qw_r, sw_r, rr.ravel(), cc.ravel(), "fprop")
     got = host_bf16_as_f64(y)[rows][:, cols].ravel()
     assert og.rel_frobenius(got, og.round_bf16(ref)) <= TOL
+
+
+def test_wgrad_full_size_pow2_x_operand_only(layer):
+    """dW = dY^T X at full size with dY^T max-abs 128x1 and X^T power-of-two
+    128x1 (pow2_operands = B), FP32 out, sampled entries."""
+    fp8q = require_gpu()
+    d = layer
+    dy = output_grad()["dy"]
+    qdyt, sdy = fp8q.fp8_quant_tile(dev_bf16(dy), fp8q.TILE_128x1, fp8q.MAXABS)
+    qxt, sx = fp8q.fp8_quant_tile(dev_bf16(d["x"]), fp8q.TILE_128x1, fp8q.POW2)
+    dw = fp8q.fp8_gemm_blockscaled_pow2(2, qdyt, sdy, qxt, sx, out_dtype=torch.float32, pow2_operands=fp8q.POW2_B)
+    rng = np.random.default_rng(185)
+    ms = np.sort(rng.choice(18432, 24, replace=False))
+    ns = np.sort(rng.choice(7168, 40, replace=False))
+    qa_r, sa_r = oq.quant_128x1(oq.bf16_bits_to_f32(dy[:, ms]), "maxabs")
+    qb_r, sb_r = oq.quant_128x1(oq.bf16_bits_to_f32(d["x"][:, ns]), "pow2")
+    rr, cc = np.meshgrid(np.arange(ms.size), np.arange(ns.size), indexing="ij")
+    ref = og.gemm_ref_entries(qa_r, sa_r, qb_r, sb_r, rr.ravel(), cc.ravel(), "wgrad")
+    got = host(dw)[ms][:, ns].ravel().astype(np.float64)
+    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= TOL
 
 
 def test_pow2_wgrad_full_size_sampled(layer):
