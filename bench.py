@@ -184,7 +184,7 @@ def cpu_baseline():
     from threadpoolctl import threadpool_info
     from oracle import gemm as og, quant as oq
     from workloads import bf16_bits_as_f32, linear_layer
-    m, n = 2048, 12288
+    m, n = 3072, 12288
     d = linear_layer()
     x = bf16_bits_as_f32(d["x"][:m])
     wt = bf16_bits_as_f32(d["wt"][:n])
