@@ -87,11 +87,6 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   v = FP8Q_DPP_MAX(v, 0x140);
   return v;
 }
-__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
-  v = FP8Q_DPP_MAX(v, 0xB1);
-  v = FP8Q_DPP_MAX(v, 0x4E);
-  return v;
-}
 
 __device__ __forceinline__ float clamp448(float v) {
   return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);

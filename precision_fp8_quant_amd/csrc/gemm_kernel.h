@@ -80,10 +80,7 @@ __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + 
 // B tiles are stored in LDS in fragment order: LDS row rho = 64*p + 16*js + r
 // holds global row 64*p + 16*(r/4) + 4*js + r%4, so the 16 rows a fragment
 // needs are consecutive in LDS while a lane still ends up owning 16
-// consecutive output columns.
-__device__ __forceinline__ int b_row_of_lds_row(int rho) {
-  return (rho & ~63) | (((rho & 15) >> 2) << 4) | (((rho >> 4) & 3) << 2) | (rho & 3);
-}
+// consecutive output columns (the B DMA below writes this order).
 
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;

@@ -3,12 +3,13 @@
 //  * 1x128 tiles (one token x 128 channels), scales [cols/128][rows]
 //  * 128x1 tiles (128 tokens x one channel), codes written transposed
 //  * 128x128 blocks (weights), optional transposed copy for Dgrad
+//  * FP8 -> FP8 re-tiling of 1x128 codes into 128x1 tiles (backward pass)
 //
 // Tile shapes and the max-abs -> scale -> cast sequence: dssusan.co.kr FP8
 // excerpt, paragraphs 2 and 4; "Deepseek - Not For everyone", paragraph 3;
 // power-of-2 scales: dssusan.co.kr FP8 excerpt, paragraph 1.
 //
-// All three kernels are HBM-bound streaming passes: 16-byte coalesced loads,
+// All four kernels are HBM-bound streaming passes: 16-byte coalesced loads,
 // max-abs taken on the integer bit patterns of |x| (non-negative floats order
 // like their bits; BF16 pairs reduce two at a time with v_pk_max_u16),
 // reduced across lanes with DPP (and LDS across waves where a group spans
