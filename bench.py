@@ -88,6 +88,18 @@ class Step:
         self.gmap = torch.from_numpy(moe["group_of_mtile"]).cuda()
         self.moe_tokens = int(moe["counts"].sum())
         self.m_pad = moe["x"].shape[0]
+        # per-expert roofline of the grouped GEMM: each expert's time is bounded by
+        # its FLOP at the MFMA peak or its bytes (codes, scales, its weights, BF16
+        # output of its padded rows) at the HBM peak, whichever is larger
+        roof_s = 0.0
+        for cnt, pad in zip(moe["counts"], moe["padded"]):
+            if pad == 0:
+                continue
+            flop = 2.0 * int(cnt) * N_MOE * D_IN
+            nbytes = pad * D_IN + pad * (D_IN // 128) * 4 + N_MOE * D_IN + (N_MOE // 128) * (D_IN // 128) * 4 \
+                + pad * N_MOE * 2
+            roof_s += max(flop / (PEAK_FP8_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+        self.grouped_roof_us = roof_s * 1e6
         del lin, dy, moe
         dev = self.x.device
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
@@ -264,6 +276,10 @@ def main():
     per_kernel["calibration copy 1 GiB"] = dict(_kernel_entry(float(np.median(cps)), 2 << 30, "bytes"),
                                                 outside_step=True)
     del src, dst
+
+    g = per_kernel["gemm grouped MoE"]
+    g["per_expert_roof_us"] = round(step.grouped_roof_us, 1)
+    g["per_expert_roof_frac"] = round(step.grouped_roof_us / g["us"], 4)
 
     ms_per_step = elapsed / args.steps * 1e3
     value = step.step_flop / (elapsed / args.steps) / 1e12
