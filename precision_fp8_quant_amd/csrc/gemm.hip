@@ -10,7 +10,7 @@ hipError_t launch_gemm(int kind, int64_t M, int64_t N, int64_t K,
                        const uint8_t* a, int64_t lda, const float* sa,
                        const uint8_t* b, int64_t ldb, const float* sb,
                        void* c, bool out_bf16, int64_t ldc, bool accumulate, hipStream_t st) {
-  GemmArgs args{a, lda, sa, b, ldb, sb, c, ldc, M, N, K, nullptr, 0, 0, 0};
+  GemmArgs args{a, lda, sa, b, ldb, sb, c, ldc, M, N, K, nullptr, 0, 0, 0, M};
   const int out = out_code(out_bf16, accumulate);
   if (kind == 2) return launch_out<kScaleRow, false, kHwNone>(args, out, st);
   return launch_out<kScaleBlock, false, kHwNone>(args, out, st);
@@ -22,7 +22,7 @@ hipError_t launch_gemm_pow2_one(int kind, int pow2_operands, int64_t M, int64_t 
                                 const uint8_t* a, int64_t lda, const float* sa,
                                 const uint8_t* b, int64_t ldb, const float* sb,
                                 void* c, bool out_bf16, int64_t ldc, bool accumulate, hipStream_t st) {
-  GemmArgs args{a, lda, sa, b, ldb, sb, c, ldc, M, N, K, nullptr, 0, 0, 0};
+  GemmArgs args{a, lda, sa, b, ldb, sb, c, ldc, M, N, K, nullptr, 0, 0, 0, M};
   const int out = out_code(out_bf16, accumulate);
   if (pow2_operands == kHwA) {
     if (kind == 2) return launch_out<kScaleRow, false, kHwA>(args, out, st);
@@ -38,7 +38,7 @@ hipError_t launch_gemm_grouped(int32_t num_groups, int64_t M_total, int64_t N, i
                                const uint8_t* b, const float* sb,
                                void* c, bool out_bf16, int64_t ldc, hipStream_t st) {
   GemmArgs args{a, lda, sa, b, K, sb, c, ldc, M_total, N, K,
-                group_of_mtile, num_groups, N * K, (N / 128) * (K / 128)};
+                group_of_mtile, num_groups, N * K, (N / 128) * (K / 128), M_total};
   return launch_out<kScaleBlock, true, kHwNone>(args, out_code(out_bf16, false), st);
 }
 

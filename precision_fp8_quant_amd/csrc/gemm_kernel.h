@@ -57,6 +57,9 @@ struct GemmArgs {
   int64_t M, N, K;
   // grouped variant
   const int32_t* group_of_mtile; int32_t num_groups; int64_t b_group_stride; int64_t sb_group_stride;
+  // leading dimension of the A scales [K/128][sa_ld] (the full M; a grid
+  // that covers a band of rows gets sa offset to its first row)
+  int64_t sa_ld;
 };
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     issue_stage(gn, stage ^ 1);
     issue_scales(gn, stage ^ 1);
 #pragma unroll
-    for (int ms = 0; ms < SM; ++ms) sa_nxt[ms] = p.sa[gn * p.M + m_lane + 16 * ms];
+    for (int ms = 0; ms < SM; ++ms) sa_nxt[ms] = p.sa[gn * p.sa_ld + m_lane + 16 * ms];
     if constexpr (BSCALE == kScaleBlock) sb_nxt = sbptr[(n_wave >> 7) * KG + gn];
 
     const uint8_t* ta = smem + stage * STAGE;
@@ -440,6 +443,28 @@ static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
 template <int BSCALE, int OUT, bool GROUPED, int HW>
 static hipError_t launch_balanced(const GemmArgs& a, hipStream_t st) {
   constexpr int64_t kCUs = 256;
+  // Grouped GEMM: the same for a last wave of 128x512 tiles, split off along
+  // M instead (whole 128-row tiles, each in one group), e.g. the 64-expert MoE
+  // layer with 543 M-tiles: 2048 + 248 tiles (8 waves + one of 128x256)
+  // instead of 2172 in 8.5 waves.
+  if constexpr (GROUPED) {
+    if (a.N % 512 == 0) {
+      const int64_t tn = a.N / 512, tiles = (a.M / 128) * tn;
+      const int64_t tail = tiles % kCUs;
+      if (tiles > kCUs && tail != 0 && 2 * tail <= kCUs && tail % tn == 0) {
+        GemmArgs head = a, rest = a;
+        rest.M = (tail / tn) * 128;
+        head.M = a.M - rest.M;
+        rest.a = a.a + head.M * a.lda;
+        rest.sa = a.sa + head.M;
+        rest.group_of_mtile = a.group_of_mtile + head.M / 128;
+        rest.c = static_cast<uint8_t*>(a.c) + head.M * a.ldc * (OUT == kOutBF16 ? 2 : 4);
+        const hipError_t e = launch_cfg<128, 512, 2, 4, BSCALE, OUT, true, HW>(head, st);
+        if (e != hipSuccess) return e;
+        return launch_cfg<128, 256, 2, 4, BSCALE, OUT, true, HW>(rest, st);
+      }
+    }
+  }
   if constexpr (BSCALE == kScaleBlock && !GROUPED) {
     if (a.M % 256 == 0 && a.N % 256 == 0) {
       const int64_t tm = a.M / 256, tiles = tm * (a.N / 256);

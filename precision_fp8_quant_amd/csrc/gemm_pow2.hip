@@ -16,7 +16,7 @@ hipError_t launch_gemm_pow2(int kind, int64_t M, int64_t N, int64_t K,
                             const uint8_t* a, int64_t lda, const float* sa,
                             const uint8_t* b, int64_t ldb, const float* sb,
                             void* c, bool out_bf16, int64_t ldc, bool accumulate, hipStream_t st) {
-  GemmArgs args{a, lda, sa, b, ldb, sb, c, ldc, M, N, K, nullptr, 0, 0, 0};
+  GemmArgs args{a, lda, sa, b, ldb, sb, c, ldc, M, N, K, nullptr, 0, 0, 0, M};
   const int out = out_bf16 ? kOutBF16 : (accumulate ? kOutF32Acc : kOutF32);
   if (kind == 2) return launch_out<kScaleRow, false, kHwAB>(args, out, st);
   return launch_out<kScaleBlock, false, kHwAB>(args, out, st);

@@ -172,6 +172,32 @@ def test_grouped_small(n):
     assert og.rel_frobenius(h[keep], ref[keep]) <= TOL_F32
 
 
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_grouped_tail_balanced_two_grid_launch(out):
+    """65 M-tiles x N=2048: 260 tiles of 128x512 on 256 CUs, so the last M-tile
+    runs as a second grid of 128x256 tiles (its A rows, A scales, group ids and
+    C rows offset); every output is checked, both grids separately."""
+    fp8q = require_gpu()
+    rng = np.random.default_rng(91)
+    g, n, k, tiles_m = 4, 2048, 256, 65
+    gmap = rng.integers(0, g, size=tiles_m).astype(np.int32)
+    gmap[-1] = 3                                   # the split-off tile uses a group of its own choosing
+    ops = random_fp8_operands(92, 128 * tiles_m, n * g, k)
+    qa, sa = ops["qa"], ops["sa"]
+    qb = ops["qb"].reshape(g, n, k)
+    sb = np.exp2(rng.uniform(-8, -2, size=(g, n // 128, k // 128))).astype(np.float32)
+    ref = og.grouped_ref(qa, sa, qb, sb, gmap)
+    if out == "bf16":
+        c = fp8q.fp8_gemm_blockscaled_grouped(dev(gmap), dev(qa), dev(sa), dev(qb), dev(sb))
+        got, want, tol = host_bf16_as_f64(c), og.round_bf16(ref), TOL
+    else:
+        c = torch.empty((128 * tiles_m, n), dtype=torch.float32, device="cuda")
+        fp8q.fp8_gemm_blockscaled_grouped(dev(gmap), dev(qa), dev(sa), dev(qb), dev(sb), c=c)
+        got, want, tol = host(c).astype(np.float64), ref, TOL_F32
+    for rows in (slice(0, 128 * 64), slice(128 * 64, 128 * tiles_m)):   # first grid, second grid
+        assert og.rel_frobenius(got[rows], want[rows]) <= tol, rows
+
+
 # ----------------------------------------------------------------------------
 # Full-size workloads: GPU quantizes and multiplies; the oracle quantizes the
 # sampled rows / bands itself from the same seeded inputs and recomputes the
@@ -267,6 +293,7 @@ def test_grouped_full_size_sampled():
     gmap = d["group_of_mtile"]
     rng = np.random.default_rng(84)
     tiles = np.sort(rng.choice(gmap.size, 6, replace=False))
+    tiles = np.unique(np.append(tiles, gmap.size - 1))               # the last M-tile runs in the tail grid
     bands = [0, 9]
     cols = np.concatenate([b * 128 + np.sort(rng.choice(128, 32, replace=False)) for b in bands])
     yh = host_bf16_as_f64(y)
