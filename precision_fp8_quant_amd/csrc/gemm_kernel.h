@@ -133,8 +133,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   const int64_t tiles_m = p.M / BM;
   const int64_t tiles_n = p.N / BN;
   const int64_t ntiles = tiles_m * tiles_n;
+  // Workgroup i runs on XCD i % 8: give every XCD one contiguous range of
+  // tiles (ceil or floor of ntiles/8), so neighbouring tiles share its L2.
   int64_t bid = blockIdx.x;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);   // neighbouring tiles share an XCD
+  {
+    const int64_t q = ntiles >> 3, r = ntiles & 7, x = bid & 7, l = bid >> 3;
+    bid = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + l;
+  }
   constexpr int64_t GROUP_M = 8;
   const int64_t per_group = GROUP_M * tiles_n;
   const int64_t first_m = (bid / per_group) * GROUP_M;
