@@ -322,9 +322,14 @@ template <int MODE>
 __global__ __launch_bounds__(256) void requant_128x1_kernel(
     const uint8_t* __restrict__ q, int64_t rows, int64_t cols, int64_t ld_q,
     const float* __restrict__ s_in, uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ s_out) {
-  __shared__ uint32_t part[16 * kRqPartPitch];
+  // The column partials (steps 2-3) and the transposed tile (step 4) are live
+  // at different times, between barriers, and share one LDS buffer.
+  constexpr int kPartWords = 16 * kRqPartPitch;
+  constexpr int kTileWords = 128 * kT1Pitch / 4;
+  __shared__ uint32_t buf[kPartWords > kTileWords ? kPartWords : kTileWords];
   __shared__ float inv_s[128];
-  __shared__ uint32_t tile[128 * kT1Pitch / 4];
+  uint32_t* const part = buf;
+  uint32_t* const tile = buf;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -344,24 +349,20 @@ __global__ __launch_bounds__(256) void requant_128x1_kernel(
     w[j] = *reinterpret_cast<const u32x4*>(q + (row0 + q4 * 4 + j) * ld_q + col0 + c8 * 16);
   const v4f sr = *reinterpret_cast<const v4f*>(s_in + cg * rows + row0 + q4 * 4);
 
-  float x[4][16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[j][d]), false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[j][d]), true);
-      x[j][4 * d + 0] = lo[0] * sr[j];
-      x[j][4 * d + 1] = lo[1] * sr[j];
-      x[j][4 * d + 2] = hi[0] * sr[j];
-      x[j][4 * d + 3] = hi[1] * sr[j];
-    }
+  // Dequantized value i (column c8*16 + i) of row j: decoded again where it is
+  // needed instead of held (keeps the kernel at 8 waves per SIMD).
+  auto deq = [&](int j, int i) {
+    const int word = int(w[j][i >> 2]);
+    const auto pr = ((i >> 1) & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
+                                   : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+    return pr[i & 1] * sr[j];
+  };
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t b = __float_as_uint(x[j][i]) & 0x7FFFFFFFu;
+      const uint32_t b = __float_as_uint(deq(j, i)) & 0x7FFFFFFFu;
       m = b > m ? b : m;
     }
     m = FP8Q_DPP_MAX(m, 0x128);                   // row_ror:8 -> lanes l and l+8 of a DPP row
@@ -379,11 +380,15 @@ __global__ __launch_bounds__(256) void requant_128x1_kernel(
     inv_s[t] = sp.inv;
     s_out[rblk * cols + col0 + t] = sp.s;
   }
-  __syncthreads();
+  __syncthreads();                                // partials consumed: the buffer becomes the tile
+  // Opaque to the compiler: the decode below is recomputed from the 16 code
+  // registers rather than the 64 values of the first pass kept alive.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(w[j]));
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float inv = inv_s[c8 * 16 + i];
-    tile[((c8 * 16 + i) * kT1Pitch + q4 * 4) >> 2] = cvt4<MODE>(x[0][i], x[1][i], x[2][i], x[3][i], inv);
+    tile[((c8 * 16 + i) * kT1Pitch + q4 * 4) >> 2] = cvt4<MODE>(deq(0, i), deq(1, i), deq(2, i), deq(3, i), inv);
   }
   __syncthreads();
   const int cc = t >> 1;
