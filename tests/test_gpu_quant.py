@@ -109,8 +109,9 @@ def test_quant_1x128_every_bf16_pattern(mode_name, mode):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mode_name,mode", MODES)
-@pytest.mark.parametrize("shape", [(128, 8), (256, 200), (384, 64), (128, 1000)])
+@pytest.mark.parametrize("shape", [(128, 8), (256, 200), (384, 64), (128, 1000), (256, 512), (384, 264)])
 def test_quant_128x1(dtype, mode_name, mode, shape):
+    """Column counts that end in a partial 64-column tile (200, 1000, 264) and ones that do not."""
     fp8q = require_gpu()
     x_dev, x_ref = _to_dev(_data(7 + shape[1], shape), dtype)
     qt, s = fp8q.fp8_quant_tile(x_dev, fp8q.TILE_128x1, mode)
@@ -146,6 +147,20 @@ def test_quant_strided_input_and_outputs():
     q_ref, s_ref = oq.quant_1x128(oq.bf16_bits_to_f32(bits[:, 128:384]), "maxabs")
     assert_bytes_equal(host(q_store)[:, :256], q_ref, "codes")
     assert np.all(host(q_store)[:, 256:] == 0)
+    assert_bytes_equal(host(s), s_ref, "scales")
+
+
+def test_quant_128x1_strided_input_and_output():
+    """128x1 on a column slice of a wider matrix, transposed codes into a wider buffer."""
+    fp8q = require_gpu()
+    full = _data(6, (256, 768))
+    bits = to_bf16_bits(full)
+    x_dev = dev_bf16(bits)[:, 128:648]                       # ld 768, width 520
+    qt_store = torch.zeros((520, 288), dtype=torch.uint8, device="cuda")
+    qt, s = fp8q.fp8_quant_tile(x_dev, fp8q.TILE_128x1, 0, q=qt_store[:, :256])
+    qt_ref, s_ref = oq.quant_128x1(oq.bf16_bits_to_f32(bits[:, 128:648]), "maxabs")
+    assert_bytes_equal(host(qt_store)[:, :256], qt_ref, "transposed codes")
+    assert np.all(host(qt_store)[:, 256:] == 0)
     assert_bytes_equal(host(s), s_ref, "scales")
 
 
