@@ -120,18 +120,41 @@ def _ld(t):
     return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def _expect(t, name, dtype, shape, device, dense=False):
+    """Check a caller-provided tensor before its pointer reaches the C ABI, which
+    cannot see sizes: device, dtype, exact logical shape, and layout (dense, or
+    2-D row-major with a leading dimension the ABI checks)."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dense:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    else:
+        _rowmajor(t, name)
+    return t
+
+
 def fp8_quant_tile(x, tile=TILE_1x128, mode=MAXABS, q=None, scales=None, stream=None):
     """1x128 (q[rows][cols], scales[cols/128][rows]) or 128x1 (q[cols][rows] transposed,
     scales[rows/128][cols]) quantization of a 2-D bf16/fp32 tensor."""
     _rowmajor(x, "x")
     rows, cols = x.shape
+    q_shape = (rows, cols) if tile == TILE_1x128 else (cols, rows)
+    s_shape = (_cdiv(cols, 128), rows) if tile == TILE_1x128 else (_cdiv(rows, 128), cols)
     if q is None:
-        shape = (rows, cols) if tile == TILE_1x128 else (cols, rows)
-        q = torch.empty(shape, dtype=torch.uint8, device=x.device)
+        q = torch.empty(q_shape, dtype=torch.uint8, device=x.device)
     if scales is None:
-        shape = (cols // 128, rows) if tile == TILE_1x128 else (rows // 128, cols)
-        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
-    q = _codes(q)
+        scales = torch.empty(s_shape, dtype=torch.float32, device=x.device)
+    q = _expect(_codes(q), "q", torch.uint8, q_shape, x.device)
+    _expect(scales, "scales", torch.float32, s_shape, x.device, dense=True)
     _check(lib.fp8_quant_tile(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), tile, mode,
                               q.data_ptr(), _ld(q), scales.data_ptr(), _stream(stream)))
     return q, scales
@@ -153,8 +176,13 @@ def fp8_quant_block(w, mode=MAXABS, transposed=False, q=None, scales=None, q_t=N
             q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
         if scales_t is None:
             scales_t = torch.empty((cols // 128, rows // 128), dtype=torch.float32, device=dev)
-    q = _codes(q)
-    qt_ptr = _codes(q_t).data_ptr() if q_t is not None else None
+    q = _expect(_codes(q), "q", torch.uint8, (rows, cols), dev)
+    _expect(scales, "scales", torch.float32, (_cdiv(rows, 128), _cdiv(cols, 128)), dev, dense=True)
+    if q_t is not None:
+        q_t = _expect(_codes(q_t), "q_t", torch.uint8, (cols, rows), dev)
+    if scales_t is not None:
+        _expect(scales_t, "scales_t", torch.float32, (_cdiv(cols, 128), _cdiv(rows, 128)), dev, dense=True)
+    qt_ptr = q_t.data_ptr() if q_t is not None else None
     ld_qt = _ld(q_t) if q_t is not None else 0
     st_ptr = scales_t.data_ptr() if scales_t is not None else None
     _check(lib.fp8_quant_block(w.data_ptr(), _dtype_code(w), rows, cols, _ld(w), mode,
@@ -185,9 +213,17 @@ def _gemm(fn, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream, 
     n = b.shape[0]
     if b.shape[1] != k:
         raise ValueError("a and b disagree on K")
+    dev = a.device
+    _expect(b, "b", torch.uint8, (n, k), dev)
+    if kind in (FPROP, DGRAD, WGRAD):              # any other kind is the ABI's FP8Q_ERR_ARG
+        _expect(a_scales, "a_scales", torch.float32, (_cdiv(k, 128), m), dev, dense=True)
+        sb_shape = (_cdiv(k, 128), n) if kind == WGRAD else (_cdiv(n, 128), _cdiv(k, 128))
+        _expect(b_scales, "b_scales", torch.float32, sb_shape, dev, dense=True)
     if c is None:
-        c = torch.empty((m, n), dtype=out_dtype, device=a.device)
-    _rowmajor(c, "c")
+        c = torch.empty((m, n), dtype=out_dtype, device=dev)
+    if c.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"c must be bfloat16 or float32, got {c.dtype}")
+    _expect(c, "c", c.dtype, (m, n), dev)
     _check(fn(kind, m, n, k, a.data_ptr(), _ld(a), a_scales.data_ptr(), b.data_ptr(), _ld(b), b_scales.data_ptr(),
               c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0, *extra, _stream(stream)))
     return c
@@ -205,10 +241,16 @@ def fp8_gemm_blockscaled_grouped(group_of_mtile, a, a_scales, b, b_scales, out_d
     m = a.shape[0]
     if a.shape[1] != k:
         raise ValueError("a and b disagree on K")
-    if group_of_mtile.dtype != torch.int32 or not group_of_mtile.is_cuda:
-        raise ValueError("group_of_mtile must be a device int32 tensor")
+    dev = a.device
+    _expect(b, "b", torch.uint8, (g, n, k), dev, dense=True)
+    _expect(group_of_mtile, "group_of_mtile", torch.int32, (_cdiv(m, 128),), dev, dense=True)
+    _expect(a_scales, "a_scales", torch.float32, (_cdiv(k, 128), m), dev, dense=True)
+    _expect(b_scales, "b_scales", torch.float32, (g, _cdiv(n, 128), _cdiv(k, 128)), dev, dense=True)
     if c is None:
-        c = torch.empty((m, n), dtype=out_dtype, device=a.device)
+        c = torch.empty((m, n), dtype=out_dtype, device=dev)
+    if c.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"c must be bfloat16 or float32, got {c.dtype}")
+    _expect(c, "c", c.dtype, (m, n), dev)
     _check(lib.fp8_gemm_blockscaled_grouped(g, m, n, k, group_of_mtile.data_ptr(), a.data_ptr(), _ld(a),
                                             a_scales.data_ptr(), b.data_ptr(), b_scales.data_ptr(),
                                             c.data_ptr(), _dtype_code(c), _ld(c), _stream(stream)))
@@ -221,11 +263,13 @@ def fp8_requant_1x128_to_128x1(q, scales, mode=POW2, q_t=None, scales_t=None, st
     q = _codes(_rowmajor(q, "q"))
     rows, cols = q.shape
     dev = q.device
+    _expect(scales, "scales", torch.float32, (_cdiv(cols, 128), rows), dev, dense=True)
     if q_t is None:
         q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
     if scales_t is None:
-        scales_t = torch.empty((rows // 128, cols), dtype=torch.float32, device=dev)
-    q_t = _codes(q_t)
+        scales_t = torch.empty((_cdiv(rows, 128), cols), dtype=torch.float32, device=dev)
+    q_t = _expect(_codes(q_t), "q_t", torch.uint8, (cols, rows), dev)
+    _expect(scales_t, "scales_t", torch.float32, (_cdiv(rows, 128), cols), dev, dense=True)
     _check(lib.fp8_requant_1x128_to_128x1(q.data_ptr(), rows, cols, _ld(q), scales.data_ptr(), mode,
                                           q_t.data_ptr(), _ld(q_t), scales_t.data_ptr(), _stream(stream)))
     return q_t, scales_t

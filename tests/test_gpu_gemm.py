@@ -113,15 +113,17 @@ def test_wgrad_accumulate_into_fp32():
 
 def test_k_zero_writes_zeros_and_empty_is_noop():
     fp8q = require_gpu()
+    f32 = dict(dtype=torch.float32, device="cuda")
     a = torch.zeros((128, 0), dtype=torch.uint8, device="cuda")
     b = torch.zeros((256, 0), dtype=torch.uint8, device="cuda")
-    s = torch.zeros((1,), dtype=torch.float32, device="cuda")
-    c = torch.full((128, 256), 7.0, dtype=torch.float32, device="cuda")
-    fp8q.fp8_gemm_blockscaled(0, a, s, b, s, c=c)
+    c = torch.full((128, 256), 7.0, **f32)
+    # K = 0: the scale arrays [K/128][M] and [N/128][K/128] are empty
+    fp8q.fp8_gemm_blockscaled(0, a, torch.zeros((0, 128), **f32), b, torch.zeros((2, 0), **f32), c=c)
     assert torch.all(c == 0).item()
-    e = torch.full((0, 256), 1.0, dtype=torch.float32, device="cuda")
-    fp8q.fp8_gemm_blockscaled(0, torch.zeros((0, 128), dtype=torch.uint8, device="cuda"), s,
-                              torch.zeros((256, 128), dtype=torch.uint8, device="cuda"), s, c=e)
+    e = torch.full((0, 256), 1.0, **f32)
+    fp8q.fp8_gemm_blockscaled(0, torch.zeros((0, 128), dtype=torch.uint8, device="cuda"), torch.zeros((1, 0), **f32),
+                              torch.zeros((256, 128), dtype=torch.uint8, device="cuda"), torch.zeros((2, 1), **f32),
+                              c=e)
 
 
 def test_gemm_deterministic():
