@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "FP8 block-scaled GEMM TFLOP/s & % FP8 MFMA peak; quantizer GB/s (1 GPU)"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+PEAK_CLOCK_GHZ = 2.4          # the engine clock the published MFMA peak assumes
 
 T, D_IN, D_OUT = 8192, 7168, 18432
 G_MOE, N_MOE = 64, 2048
@@ -327,17 +328,26 @@ def _kernel_entry(us, work, kind):
 
 
 def _roofline(name, k):
-    traffic = None
+    """Roofline entry of the dominant kernel.  traffic (calibrated HBM bytes per launch) and, for an MFMA-bound
+    kernel, its average shader clock come from profiles/hbm_traffic.json, and only while that file's kernel
+    source hash matches; frac_at_clock sets the achieved rate against the published peak scaled from its
+    2.4 GHz to that clock."""
+    traffic, clock = None, None
     tpath = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if os.path.exists(tpath):
         with open(tpath) as fh:
             t = json.load(fh)
-        if t.get("source_hash") == source_hash() and name in t.get("kernels", {}):
-            traffic = t["kernels"][name]
+        if t.get("source_hash") == source_hash():
+            traffic = t.get("kernels", {}).get(name)
+            clock = t.get("clock_ghz", {}).get(name)
     if "tflops" in k:
-        return {"kernel": name, "bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(k["tflops"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
-                "avg_us": k["us"]}
+        r = {"kernel": name, "bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(k["tflops"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+             "avg_us": k["us"]}
+        if clock:
+            r["clock_ghz"] = clock
+            r["frac_at_clock"] = round(k["tflops"] / (PEAK_FP8_TFLOPS * clock / PEAK_CLOCK_GHZ), 4)
+        return r
     return {"kernel": name, "bound": "hbm", "achieved": k["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(k["gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic, "avg_us": k["us"]}
 
