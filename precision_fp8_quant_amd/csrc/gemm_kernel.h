@@ -173,19 +173,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   const uint8_t* a_base = p.a + m0 * p.lda;
   const uint8_t* b_base = bptr + n0 * p.ldb;
 
-  auto issue_stage = [&](int64_t g, int stage) {
+  // DMA instruction i (0 .. A_DMA+B_DMA-1) of this wave's share of group g.
+  auto issue_dma = [&](int64_t g, int stage, int i) {
     uint8_t* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
+    if (i < A_DMA) {
       const int blk = wave_u * A_DMA + i;
       dma16(a_base + int64_t(8 * blk) * p.lda + g * 128 + a_off, base + blk * 1024);
-    }
-#pragma unroll
-    for (int i = 0; i < B_DMA; ++i) {
-      const int blk = wave_u * B_DMA + i;
+    } else {
+      const int blk = wave_u * B_DMA + (i - A_DMA);
       const int row_u = 64 * (blk >> 3) + 32 * (blk & 1) + 4 * ((blk >> 1) & 3);
       dma16(b_base + int64_t(row_u) * p.ldb + g * 128 + b_off, base + A_BYTES + blk * 1024);
     }
+  };
+  auto issue_stage = [&](int64_t g, int stage) {
+#pragma unroll
+    for (int i = 0; i < A_DMA + B_DMA; ++i) issue_dma(g, stage, i);
   };
   // Per-column B scales of group g into slot `slot` (issued at the top of an
   // iteration, where a wave-uniform branch splits no MFMA/FMA block).
@@ -221,10 +223,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
         for (int d = 0; d < 4; ++d) acc[a][b][c][d] = 0.0f;
       }
 
-  // Per K-group: the DMA of group g+1 into the other stage is issued first,
-  // then the group's MFMAs run from LDS fragments, then one barrier.  Inside
-  // the group a software pipeline over its NT = NB*SM MFMAs (step t: B
-  // fragment bi = t/SM against A fragment ms = t%SM):
+  // Per K-group: the group's MFMAs run from LDS fragments while the DMA of
+  // group g+1 into the other stage is issued between its first MFMAs, then
+  // one barrier.  Inside the group a software pipeline over its NT = NB*SM
+  // MFMAs (step t: B fragment bi = t/SM against A fragment ms = t%SM):
   //  * promoted path: MFMA t writes result slot t%3 and the promotion FMAs of
   //    MFMA t-2 follow it, so a VALU op never waits on the MFMA just issued;
   //  * kHwAB: the MFMA takes both E8M0 scales and accumulates in place;
@@ -243,6 +245,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   constexpr int NT = NB * SM;           // MFMAs per group
   constexpr int LAG = IN_MFMA ? 0 : 2;
   static_assert(HW == kHwNone || !GROUPED, "the hardware-scaled paths cover the plain GEMMs");
+  static_assert(A_DMA + B_DMA <= NT, "the next group's DMA rides on this group's first MFMA steps");
 
   auto frag_row_b = [&](int bi) { return wn * TN + 16 * bi + lr; };
   auto sbq_off = [&](int bi) { return (wn * TN + 64 * (bi >> 2) + 16 * lq + 4 * (bi & 3)) * 4; };
@@ -272,7 +275,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   for (int64_t g = 0; g < KG; ++g) {
     const int stage = int(g & 1);
     const int64_t gn = g + 1 < KG ? g + 1 : g;
-    issue_stage(gn, stage ^ 1);
     issue_scales(gn, stage ^ 1);
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) sa_nxt[ms] = p.sa[gn * p.sa_ld + m_lane + 16 * ms];
@@ -340,6 +342,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
           if constexpr (!B_HW && BSCALE == kScaleRow)
             if (bi + 1 < NB) sbq[(bi + 1) % 3] = *reinterpret_cast<const v4f*>(ts + sbq_off(bi + 1));
         }
+        // the next group's DMA, one instruction after each of the group's
+        // first MFMAs: issued all at the top of the group it held back the
+        // first MFMAs (measured 3-6% slower; one every 2 MFMAs sat in between,
+        // spread over the whole group it was 5% slower still, the last
+        // instructions then landing late for the end-of-group wait)
+        if (t < A_DMA + B_DMA) issue_dma(gn, stage ^ 1, t);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (!IN_MFMA && t >= LAG) {
