@@ -150,3 +150,28 @@ def random_fp8_operands(seed, m, n, k, kind="fprop", scale_lo=2.0 ** -12, scale_
     else:
         sb = np.exp2(expo(rng.uniform(lo, hi, size=(-(-n // GROUP), g)))).astype(np.float32)
     return {"qa": qa, "sa": sa, "qb": qb, "sb": sb}
+
+
+# ----------------------------------------------------------------------------
+# Device-side draws for tensors too large to stage through the host (beyond
+# 2^31 elements); the tests copy the sampled parts back for the oracle.
+# ----------------------------------------------------------------------------
+
+def device_normal_bf16(seed, shape, sigma=1.0):
+    """sigma * N(0,1) drawn on the GPU by torch's seeded CUDA generator, rounded to BF16."""
+    torch = _torch()
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x
+
+
+def device_fp8_codes(seed, shape):
+    """Uniform random bytes drawn on the GPU; the two NaN codes (0x7F, 0xFF) are
+    moved to their neighbours 0x7E / 0xFE, so every byte is a finite E4M3 code."""
+    torch = _torch()
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randint(0, 256, shape, generator=g, device="cuda", dtype=torch.uint8)
+    q.sub_(((q & 0x7F) == 0x7F).to(torch.uint8))    # elementwise (masked indexing fails past 2^31 elements)
+    return q
