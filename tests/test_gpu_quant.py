@@ -136,6 +136,33 @@ def test_quant_block(dtype, mode_name, mode, shape):
     assert_bytes_equal(host(q2), q_ref, "codes without the transposed copy")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode_name,mode", MODES)
+def test_degenerate_groups_128x1_and_blocks(dtype, mode_name, mode):
+    """All-zero, negative-zero, constant, lone-subnormal-max and near-FP32-max groups in the 128x1 and the
+    128x128 quantizers (the scale floor and the extremes of the scale derivation)."""
+    fp8q = require_gpu()
+    x = _data(41, (256, 768))
+    x[0:128, 0:128] = 0.0                            # a 128x128 block and 128 columns of 128x1 groups: zero
+    x[128:256, 0:128] = -0.0
+    x[0:128, 128:256] = np.float32(-0.02)            # constant
+    x[128:256, 128:256] = 0.0
+    x[130, 200] = np.float32(1e-40)                  # lone FP32 subnormal as max-abs (flushes in BF16)
+    x[0:128, 256:384] = np.float32(1e30)             # near the top of the FP32 range
+    x[5, 300] = np.float32(3e38)
+    x_dev, x_ref = _to_dev(x, dtype)
+    qt, st = fp8q.fp8_quant_tile(x_dev, fp8q.TILE_128x1, mode)
+    qt_ref, st_ref = oq.quant_128x1(x_ref, mode_name)
+    assert_bytes_equal(host(st), st_ref, "128x1 scales")
+    assert_bytes_equal(host(qt), qt_ref, "128x1 codes")
+    q, s, q_t, s_t = fp8q.fp8_quant_block(x_dev, mode, transposed=True)
+    q_ref, s_ref = oq.quant_128x128(x_ref, mode_name)
+    assert_bytes_equal(host(s), s_ref, "block scales")
+    assert_bytes_equal(host(q), q_ref, "block codes")
+    assert_bytes_equal(host(q_t), q_ref.T, "transposed block codes")
+    assert_bytes_equal(host(s_t), s_ref.T, "transposed block scales")
+
+
 def test_quant_strided_input_and_outputs():
     """Leading dimensions larger than the logical width (a column slice)."""
     fp8q = require_gpu()
