@@ -430,7 +430,7 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
 //   256x256, 8 waves (4 along M x 2 along N) of 64x128
 //   grouped GEMMs (one group per 128-row tile): 128x512, 8 waves (2x4) of
 //   64x128 -- the same wave tile as 256x256, with both stages filling the
-//   160 KB of LDS (measured 7% faster than 128x256 on the MoE layer); else
+//   160 KB of LDS (measured 25% faster than 128x256 on the MoE layer); else
 //   128x256, 8 waves (2x4) of 64x64
 //   128x256, 4 waves (2x2) of 64x128
 //   256x128, 4 waves (4x1) of 64x128
