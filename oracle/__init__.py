@@ -23,7 +23,8 @@ DeepSeek-V3 FP8 material collected for this method):
 
 Modules:
     e4m3   -- OCP E4M3FN decode/encode (all pinned).
-    quant  -- 1x128, 128x1 and 128x128 quantizers, max-abs and pow2 modes (all pinned).
+    quant  -- 1x128, 128x1 and 128x128 quantizers, max-abs and pow2 modes, and the
+              FP8 -> FP8 1x128 -> 128x1 re-quantization (all pinned).
     gemm   -- block-scaled GEMM reference for Fprop/Dgrad/Wgrad and the grouped
               variant, plus output rounding to FP32/BF16 (all pinned).
     study  -- quantization-error study of the scaling rules (per-tensor,
