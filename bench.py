@@ -2,10 +2,11 @@
 
 One step = every stage of the path over one batch of synthetic input:
   * FP8 Linear layer, 8192 tokens, 7168 -> 18432 channels, forward + backward:
-      1x128 quantization of X (bf16) and of dY (bf16),
+      1x128 and 128x1 quantization of X (bf16) in one pass (1x128 for
+        Fprop, 128x1 kept for Wgrad), the same for dY (1x128 for Dgrad,
+        128x1 for Wgrad),
       128x128 quantization of the weight (bf16, stored [out][in]) with its
         transposed copy for Dgrad,
-      128x1 quantization of dY and X for Wgrad,
       Fprop  Y  = X W       (M=8192,  N=18432, K=7168,  BF16 out),
       Dgrad  dX = dY W^T    (M=8192,  N=7168,  K=18432, BF16 out),
       Wgrad  dW = dY^T X    (M=18432, N=7168,  K=8192,  FP32 out);
@@ -18,10 +19,11 @@ TFLOP/s; every kernel of the step is inside the timed region.  Per-kernel
 durations come from HIP events recorded on the stream the kernels run on.
 
 After the timed steps, kernels outside the step are timed one by one (their
-entries carry "outside_step"): the power-of-two scale mode of the activation
-and weight quantizers, the FP8 -> FP8 1x128 -> 128x1 re-quantization of the
-activation, and the Fprop and Wgrad GEMMs on power-of-two operands through
-the hardware-scaled MFMA path.
+entries carry "outside_step"): the single-tiling 1x128 and 128x1 quantizers
+of dY (what the one-pass quantizer replaces), the power-of-two scale mode of
+the activation and weight quantizers, the FP8 -> FP8 1x128 -> 128x1
+re-quantization of the activation, and the Fprop and Wgrad GEMMs on
+power-of-two operands through the hardware-scaled MFMA path.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--copy-calibration]
@@ -124,26 +126,25 @@ class Step:
         self.qdyt_p2, self.sdyt_p2 = e((D_OUT, T), u8), e((T // 128, D_OUT), f32)
 
         bf16_quant_bytes = lambda r, c: r * c * 2 + r * c + (r * c // 128) * 4      # in + codes + scales
+        dual_bytes = lambda r, c: r * c * 2 + 2 * r * c + 2 * (r * c // 128) * 4    # in + both tilings
         block_bytes = lambda r, c, t: r * c * 2 + r * c * (2 if t else 1) + (r // 128) * (c // 128) * 4 * (2 if t else 1)
         gf = lambda m, n, k: 2.0 * m * n * k
         # (name, launch fn, algorithmic work, kind of work)
         q = fp8q
         self.kernels = [
-            ("quant_1x128 X", lambda: q.fp8_quant_tile(self.x, q.TILE_1x128, q.MAXABS, self.qx, self.sx),
-             bf16_quant_bytes(T, D_IN), "bytes"),
+            ("quant 1x128+128x1 X", lambda: q.fp8_quant_tile_dual(self.x, q.MAXABS, self.qx, self.sx, self.qxt,
+                                                                  self.sxt),
+             dual_bytes(T, D_IN), "bytes"),
             ("quant_128x128 W (+transposed)", lambda: q.fp8_quant_block(self.wt, q.MAXABS, True, self.qw, self.sw,
                                                                        self.qwt, self.swt),
              block_bytes(D_OUT, D_IN, True), "bytes"),
             ("gemm Fprop", lambda: q.fp8_gemm_blockscaled(q.FPROP, self.qx, self.sx, self.qw, self.sw, c=self.y),
              gf(T, D_OUT, D_IN), "flop"),
-            ("quant_1x128 dY", lambda: q.fp8_quant_tile(self.dy, q.TILE_1x128, q.MAXABS, self.qdy, self.sdy),
-             bf16_quant_bytes(T, D_OUT), "bytes"),
+            ("quant 1x128+128x1 dY", lambda: q.fp8_quant_tile_dual(self.dy, q.MAXABS, self.qdy, self.sdy,
+                                                                   self.qdyt, self.sdyt),
+             dual_bytes(T, D_OUT), "bytes"),
             ("gemm Dgrad", lambda: q.fp8_gemm_blockscaled(q.DGRAD, self.qdy, self.sdy, self.qwt, self.swt, c=self.dx),
              gf(T, D_IN, D_OUT), "flop"),
-            ("quant_128x1 dY", lambda: q.fp8_quant_tile(self.dy, q.TILE_128x1, q.MAXABS, self.qdyt, self.sdyt),
-             bf16_quant_bytes(T, D_OUT), "bytes"),
-            ("quant_128x1 X", lambda: q.fp8_quant_tile(self.x, q.TILE_128x1, q.MAXABS, self.qxt, self.sxt),
-             bf16_quant_bytes(T, D_IN), "bytes"),
             ("gemm Wgrad", lambda: q.fp8_gemm_blockscaled(q.WGRAD, self.qdyt, self.sdyt, self.qxt, self.sxt, c=self.dw),
              gf(D_OUT, D_IN, T), "flop"),
             ("quant_1x128 MoE tokens", lambda: q.fp8_quant_tile(self.mx, q.TILE_1x128, q.MAXABS, self.qmx, self.smx),
@@ -156,6 +157,13 @@ class Step:
              gf(self.moe_tokens, N_MOE, D_IN), "flop"),
         ]
         self.extra = [
+            # the two single-tiling calls that the one-pass quantizer of dY replaces (same outputs)
+            ("quant_1x128 dY (single tiling)", lambda: q.fp8_quant_tile(self.dy, q.TILE_1x128, q.MAXABS, self.qdy,
+                                                                         self.sdy),
+             bf16_quant_bytes(T, D_OUT), "bytes"),
+            ("quant_128x1 dY (single tiling)", lambda: q.fp8_quant_tile(self.dy, q.TILE_128x1, q.MAXABS,
+                                                                         self.qdyt, self.sdyt),
+             bf16_quant_bytes(T, D_OUT), "bytes"),
             ("quant_1x128 X (pow2 scales)", lambda: q.fp8_quant_tile(self.x, q.TILE_1x128, q.POW2,
                                                                      self.pow2_q, self.pow2_s),
              bf16_quant_bytes(T, D_IN), "bytes"),

@@ -118,6 +118,31 @@ int fp8_quant_block(const void* w, int w_dtype, int64_t rows, int64_t cols, int6
                     void* stream);
 
 /*
+ * fp8_quant_tile_dual -- both tilings of one tensor in one pass: the 1x128
+ * tiles of fp8_quant_tile(FP8Q_TILE_1x128) and the transposed 128x1 tiles of
+ * fp8_quant_tile(FP8Q_TILE_128x1), read from X once.
+ * [dssusan.co.kr FP8 excerpt, paragraph 4: the backward pass feeds the
+ *  output gradient to Dgrad in 1x128 tiles and to Wgrad in 128x1 tiles]
+ *
+ * x        : input X[rows][cols], leading dimension ld_x (elements), dtype x_dtype.
+ * q        : 1x128 codes q[rows][cols], leading dimension ld_q (bytes).
+ * scales   : 1x128 scales[cols/128][rows], packed.
+ * q_t      : 128x1 codes, transposed: q_t[cols][rows], leading dimension ld_qt
+ *            (bytes); q_t[c*ld_qt + r] is the 128x1 code of X[r][c].
+ * scales_t : 128x1 scales[rows/128][cols], packed.
+ * mode     : FP8Q_SCALE_MAXABS or FP8Q_SCALE_POW2 (both tilings).
+ * Every output is bit-identical to the two fp8_quant_tile calls.  All four
+ * outputs are required (FP8Q_ERR_NULL otherwise).
+ * Requires rows % 128 == 0 and cols % 128 == 0.
+ * rows == 0 or cols == 0 is a no-op returning FP8Q_OK.
+ */
+int fp8_quant_tile_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                        int mode,
+                        uint8_t* q, int64_t ld_q, float* scales,
+                        uint8_t* q_t, int64_t ld_qt, float* scales_t,
+                        void* stream);
+
+/*
  * fp8_gemm_blockscaled -- C[M][N] (+)= A . B^T with per-128-K-group scales,
  * FP32 promotion once per K-group.
  * [dssusan.co.kr FP8 excerpt, paragraph 3; youlimart.com FP8 excerpt, paragraphs 2-3]

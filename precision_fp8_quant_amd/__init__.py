@@ -8,6 +8,7 @@ no CPU fallback.
 
 Functions keep the C names:
     fp8_quant_tile(x, tile, mode)              -> (q, scales)
+    fp8_quant_tile_dual(x, mode)               -> (q, scales, q_t, scales_t)   (1x128 and 128x1 at once)
     fp8_quant_block(w, mode, transposed)       -> (q, scales[, q_t, scales_t])
     fp8_gemm_blockscaled(kind, a, sa, b, sb)   -> c
     fp8_gemm_blockscaled_pow2(kind, a, sa, b, sb, pow2_operands) -> c   (power-of-two scales)
@@ -41,6 +42,7 @@ _ptr = ctypes.c_void_p
 SIGNATURES = {
     "fp8_quant_tile": [_ptr, _int, _i64, _i64, _i64, _int, _int, _ptr, _i64, _ptr, _ptr],
     "fp8_quant_block": [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr],
+    "fp8_quant_tile_dual": [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr],
     "fp8_gemm_blockscaled": [_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _int, _i64,
                              _int, _ptr],
     "fp8_gemm_blockscaled_pow2": [_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _i64, _ptr, _ptr, _int, _i64,
@@ -158,6 +160,30 @@ def fp8_quant_tile(x, tile=TILE_1x128, mode=MAXABS, q=None, scales=None, stream=
     _check(lib.fp8_quant_tile(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), tile, mode,
                               q.data_ptr(), _ld(q), scales.data_ptr(), _stream(stream)))
     return q, scales
+
+
+def fp8_quant_tile_dual(x, mode=MAXABS, q=None, scales=None, q_t=None, scales_t=None, stream=None):
+    """1x128 (q, scales) and transposed 128x1 (q_t, scales_t) quantization of one
+    2-D bf16/fp32 tensor in one pass; the same outputs as the two fp8_quant_tile calls."""
+    _rowmajor(x, "x")
+    rows, cols = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((_cdiv(cols, 128), rows), dtype=torch.float32, device=dev)
+    if q_t is None:
+        q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if scales_t is None:
+        scales_t = torch.empty((_cdiv(rows, 128), cols), dtype=torch.float32, device=dev)
+    q = _expect(_codes(q), "q", torch.uint8, (rows, cols), dev)
+    _expect(scales, "scales", torch.float32, (_cdiv(cols, 128), rows), dev, dense=True)
+    q_t = _expect(_codes(q_t), "q_t", torch.uint8, (cols, rows), dev)
+    _expect(scales_t, "scales_t", torch.float32, (_cdiv(rows, 128), cols), dev, dense=True)
+    _check(lib.fp8_quant_tile_dual(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), mode,
+                                   q.data_ptr(), _ld(q), scales.data_ptr(), q_t.data_ptr(), _ld(q_t),
+                                   scales_t.data_ptr(), _stream(stream)))
+    return q, scales, q_t, scales_t
 
 
 def fp8_quant_block(w, mode=MAXABS, transposed=False, q=None, scales=None, q_t=None, scales_t=None,

@@ -69,7 +69,7 @@ int check_gemm(int kind, int64_t M, int64_t N, int64_t K, const uint8_t* a, int6
 
 extern "C" {
 
-int fp8q_abi_version(void) { return 103; }
+int fp8q_abi_version(void) { return 104; }
 
 const char* fp8q_status_string(int s) {
   switch (s) {
@@ -148,6 +148,33 @@ int fp8_quant_block(const void* w, int w_dtype, int64_t rows, int64_t cols, int6
   return from_hip(fp8q::launch_quant_128x128(w, w_dtype == FP8Q_BF16, rows, cols, ld_w, mode, q, ld_q,
                                              scales, q_t, ld_qt, scales_t,
                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fp8_quant_tile_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, int mode,
+                        uint8_t* q, int64_t ld_q, float* scales,
+                        uint8_t* q_t, int64_t ld_qt, float* scales_t, void* stream) {
+  if (!dtype_ok(x_dtype)) return FP8Q_ERR_ARG;
+  if (mode != FP8Q_SCALE_MAXABS && mode != FP8Q_SCALE_POW2) return FP8Q_ERR_ARG;
+  if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8Q_OK;
+  if (!x || !q || !scales || !q_t || !scales_t) return FP8Q_ERR_NULL;
+  const int64_t es = dtype_size(x_dtype);
+  if (ld_x < cols || ld_q < cols || ld_qt < rows) return FP8Q_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || !aligned16(q_t) || !aligned16(scales_t) ||
+      (ld_x * es) % 16 || ld_q % 16 || ld_qt % 16)
+    return FP8Q_ERR_ALIGN;
+  if (rows % 128 || cols % 128) return FP8Q_ERR_UNSUPPORTED;
+  const int64_t n1 = (cols / 128) * rows, n2 = (rows / 128) * cols;
+  const Range rx = span(x, rows, cols, ld_x, es);
+  const Range outs[4] = {span(q, rows, cols, ld_q, 1), span(scales, 1, n1, n1, 4),
+                         span(q_t, cols, rows, ld_qt, 1), span(scales_t, 1, n2, n2, 4)};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(rx, outs[i])) return FP8Q_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return FP8Q_ERR_ALIAS;
+  }
+  return from_hip(fp8q::launch_quant_dual(x, x_dtype == FP8Q_BF16, rows, cols, ld_x, mode, q, ld_q, scales,
+                                          q_t, ld_qt, scales_t, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int fp8_requant_1x128_to_128x1(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q,

@@ -18,6 +18,11 @@ hipError_t launch_quant_128x128(const void* w, bool bf16, int64_t rows, int64_t 
                                 int mode, uint8_t* q, int64_t ld_q, float* scales,
                                 uint8_t* q_t, int64_t ld_qt, float* scales_t, hipStream_t st);
 
+// 1x128 (q, scales) and 128x1 (q_t, scales_t) tiles of the same input in one pass.
+hipError_t launch_quant_dual(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                             int mode, uint8_t* q, int64_t ld_q, float* scales,
+                             uint8_t* q_t, int64_t ld_qt, float* scales_t, hipStream_t st);
+
 hipError_t launch_requant_128x1(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q, const float* s_in,
                                 int mode, uint8_t* q_t, int64_t ld_qt, float* s_out, hipStream_t st);
 

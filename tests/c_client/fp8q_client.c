@@ -43,7 +43,7 @@ static int check(void) {
   uint8_t* B = (uint8_t*)0x20000000;
   float* C = (float*)0x40000000;
   float* D = (float*)0x60000000;
-  if (fp8q_abi_version() != 103) return 3;
+  if (fp8q_abi_version() != 104) return 3;
   if (strncmp(fp8q_status_string(FP8Q_ERR_ALIAS), "FP8Q_ERR_ALIAS", 14) != 0) return 4;
   EXPECT(fp8_quant_tile(A, FP8Q_BF16, 0, 256, 256, FP8Q_TILE_1x128, FP8Q_SCALE_MAXABS, B, 256, C, NULL), FP8Q_OK);
   EXPECT(fp8_quant_tile(A, FP8Q_BF16, 128, 256, 256, FP8Q_TILE_1x128, 7, B, 256, C, NULL), FP8Q_ERR_ARG);

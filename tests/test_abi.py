@@ -27,7 +27,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert names == {"fp8_quant_tile", "fp8_quant_block", "fp8_gemm_blockscaled",
+    assert names == {"fp8_quant_tile", "fp8_quant_tile_dual", "fp8_quant_block", "fp8_gemm_blockscaled",
                      "fp8_gemm_blockscaled_grouped", "fp8_requant_1x128_to_128x1",
                      "fp8_gemm_blockscaled_pow2", "fp8q_status_string",
                      "fp8q_abi_version"}
@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert fp8q.lib.fp8q_abi_version() == 103
+    assert fp8q.lib.fp8q_abi_version() == 104
     for s in range(8):
         assert fp8q.status_string(s).startswith("FP8Q_")
     assert fp8q.status_string(99) == "unknown fp8q status"
@@ -88,6 +88,34 @@ def test_quant_block_validation():
     assert _block(rows=200) == fp8q.ERR_UNSUPPORTED
     assert _block(ldq=392) == fp8q.ERR_ALIGN
     assert _block(qt=B + 16, ldqt=256, st=D) == fp8q.ERR_ALIAS  # transposed codes overlap codes
+
+
+def _dual(**kw):
+    args = dict(x=A, dt=fp8q.BF16, rows=256, cols=384, ldx=384, mode=fp8q.MAXABS, q=B, ldq=384, s=C,
+                qt=D, ldqt=256, st=0x70000000)
+    args.update(kw)
+    return fp8q.lib.fp8_quant_tile_dual(args["x"], args["dt"], args["rows"], args["cols"], args["ldx"],
+                                        args["mode"], args["q"], args["ldq"], args["s"], args["qt"], args["ldqt"],
+                                        args["st"], None)
+
+
+def test_quant_tile_dual_validation():
+    assert _dual(rows=0, x=None) == fp8q.OK and _dual(cols=0, q=None) == fp8q.OK   # empty: no-op
+    assert _dual(dt=3) == fp8q.ERR_ARG
+    assert _dual(mode=2) == fp8q.ERR_ARG
+    assert _dual(cols=-128) == fp8q.ERR_SHAPE
+    for name in ("x", "q", "s", "qt", "st"):                    # all four outputs are required
+        assert _dual(**{name: None}) == fp8q.ERR_NULL, name
+    assert _dual(ldx=256) == fp8q.ERR_SHAPE
+    assert _dual(ldq=256) == fp8q.ERR_SHAPE
+    assert _dual(ldqt=128) == fp8q.ERR_SHAPE
+    assert _dual(st=0x70000004) == fp8q.ERR_ALIGN
+    assert _dual(ldqt=264) == fp8q.ERR_ALIGN
+    assert _dual(rows=200, ldqt=208) == fp8q.ERR_UNSUPPORTED    # rows must be whole 128-row tiles
+    assert _dual(cols=264, ldx=264, ldq=272) == fp8q.ERR_UNSUPPORTED
+    assert _dual(qt=B + 4096) == fp8q.ERR_ALIAS                 # transposed codes overlap the 1x128 codes
+    assert _dual(st=C + 16) == fp8q.ERR_ALIAS                   # the two scale arrays overlap
+    assert _dual(q=A + 256) == fp8q.ERR_ALIAS                   # codes overlap the input
 
 
 def _gemm(fn="fp8_gemm_blockscaled", **kw):

@@ -34,6 +34,21 @@ def test_quant_tile_outputs_checked():
     assert q.dtype == U8 and s.shape == (3, 256)                              # FP8 codes view is accepted
 
 
+def test_quant_tile_dual_outputs_checked():
+    fp8q = require_gpu()
+    x = _t((256, 384), BF)
+    with pytest.raises(ValueError, match="q_t has shape"):
+        fp8q.fp8_quant_tile_dual(x, 0, q_t=_t((256, 384), U8))                # 128x1 codes are [cols][rows]
+    with pytest.raises(ValueError, match="scales_t has shape"):
+        fp8q.fp8_quant_tile_dual(x, 0, scales_t=_t((3, 256), F32))            # the 1x128 scale shape
+    with pytest.raises(ValueError, match="scales has shape"):
+        fp8q.fp8_quant_tile_dual(x, 0, scales=_t((2, 384), F32))              # the 128x1 scale shape
+    with pytest.raises(TypeError, match="uint8 E4M3FN codes"):
+        fp8q.fp8_quant_tile_dual(x, 0, q=_t((256, 384), BF))
+    with pytest.raises(ValueError, match="must be a 2-D row-major"):
+        fp8q.fp8_quant_tile_dual(_t((384, 256), BF).t(), 0)
+
+
 def test_quant_block_and_requant_outputs_checked():
     fp8q = require_gpu()
     w = _t((256, 384), F32)
