@@ -55,6 +55,11 @@ static int check(void) {
          FP8Q_ERR_UNSUPPORTED);                            /* 1x128 needs cols % 128 == 0 */
   EXPECT(fp8_quant_block(A, FP8Q_F32, 200, 384, 384, FP8Q_SCALE_POW2, B, 384, C, NULL, 0, NULL, NULL),
          FP8Q_ERR_UNSUPPORTED);
+  EXPECT(fp8_quant_tile_dual(A, FP8Q_BF16, 256, 384, 384, FP8Q_SCALE_MAXABS, B, 384, C, NULL, 256, D, NULL),
+         FP8Q_ERR_NULL);                                   /* both tilings' outputs are required */
+  EXPECT(fp8_quant_tile_dual(A, FP8Q_BF16, 200, 384, 384, FP8Q_SCALE_MAXABS, B, 384, C, B + 0x100000, 208, D,
+                             NULL),
+         FP8Q_ERR_UNSUPPORTED);                            /* rows must be whole 128-row tiles */
   EXPECT(fp8_gemm_blockscaled(FP8Q_FPROP, 256, 256, 512, B, 512, C, B + 0x100000, 512, D, (void*)0x70000000,
                               FP8Q_BF16, 256, 1, NULL),
          FP8Q_ERR_UNSUPPORTED);                            /* accumulate needs FP32 output */

@@ -20,7 +20,8 @@ def _bf16_rows_to_f32(t):
 
 
 def test_quantizers_beyond_2g_elements():
-    """36864 x 65536 BF16 (2.4e9 elements): 1x128 rows and 128x1 columns past element 2^31."""
+    """36864 x 65536 BF16 (2.4e9 elements): 1x128 rows and 128x1 columns past element 2^31, from the
+    single-tiling and the one-pass quantizers."""
     fp8q = require_gpu()
     rows, cols = 36864, 65536
     x = device_normal_bf16(301, (rows, cols))
@@ -35,7 +36,14 @@ def test_quantizers_beyond_2g_elements():
     qt_ref, st_ref = oq.quant_128x1(_bf16_rows_to_f32(x[:, far_cols]), "pow2")
     assert_bytes_equal(host(qt[far_cols]), qt_ref, "128x1 codes")
     assert_bytes_equal(host(st[:, far_cols]), st_ref, "128x1 scales")
-    del x, qt, st
+    q, s, qt, st = fp8q.fp8_quant_tile_dual(x, fp8q.MAXABS)                 # both tilings in one pass
+    q_ref, s_ref = oq.quant_1x128(_bf16_rows_to_f32(x[far_rows]), "maxabs")
+    assert_bytes_equal(host(q[far_rows]), q_ref, "one-pass 1x128 codes")
+    assert_bytes_equal(host(s[:, far_rows]), s_ref, "one-pass 1x128 scales")
+    qt_ref, st_ref = oq.quant_128x1(_bf16_rows_to_f32(x[:, far_cols]), "maxabs")
+    assert_bytes_equal(host(qt[far_cols]), qt_ref, "one-pass 128x1 codes")
+    assert_bytes_equal(host(st[:, far_cols]), st_ref, "one-pass 128x1 scales")
+    del x, q, s, qt, st
     torch.cuda.empty_cache()
 
 
