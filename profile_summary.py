@@ -1,0 +1,247 @@
+"""Summaries of rocprofv3 runs of ``bench.py`` for ``profiles/``.
+
+Every bench call is matched to its GPU dispatches by position: the bench's
+JSON line lists its kernels in launch order (the step's kernels, then the
+ones timed outside the step, then the 1 GiB device copy), each call of the
+C ABI launches one grid, or two when a GEMM runs its last wave as a second
+grid of 128x256 tiles, and bench.py runs every step kernel (warm-up + timed
+steps) before the outside-step ones (2 untimed + timed calls each).  Each
+figure is the mean over the timed calls.
+
+  python profile_summary.py trace BENCH_JSON TRACE_DIR --steps K
+      kernel-trace table (rocprofv3 --kernel-trace --stats) -> stdout (markdown)
+  python profile_summary.py traffic BENCH_JSON FETCH_DIR WRITE_DIR CLOCK_DIR --steps K
+      calibrated HBM bytes per launch (FETCH_SIZE, WRITE_SIZE, scaled by what the
+      counters read for the plain 1 GiB copy) and the GEMMs' average shader clock
+      (GRBM_GUI_ACTIVE / (8 XCDs x duration)) -> profiles/hbm_traffic.json + markdown on stdout
+
+BENCH_JSON is a file holding the bench's JSON line (any run of the same tree).
+"""
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+# kernel family expected for each bench name (checked on every matched dispatch)
+FAMILIES = [
+    ("requant", "requant_128x1_kernel"),
+    ("quant 1x128+128x1", "quant_dual_kernel"),
+    ("quant_128x128", "quant_128x128_kernel"),
+    ("quant_1x128", "quant_1x128_kernel"),
+    ("quant_128x1", "quant_128x1_kernel"),
+    ("gemm", "gemm_blockscaled_kernel"),
+]
+COPY = "calibration copy 1 GiB"
+XCDS = 8
+
+
+def family(bench_name):
+    for prefix, fam in FAMILIES:
+        if bench_name.startswith(prefix):
+            return fam
+    raise ValueError(f"no kernel family for bench name {bench_name!r}")
+
+
+def is_second_grid(kernel_name):
+    """The 128x256 grid that a GEMM call launches after its first grid."""
+    return "gemm_blockscaled_kernel<128, 256, 2, 4," in kernel_name
+
+
+def read_bench(path):
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("{"):
+                return json.loads(line)
+    raise ValueError(f"no JSON line in {path}")
+
+
+def read_csv(d, suffix):
+    files = glob.glob(os.path.join(d, "**", f"*_{suffix}.csv"), recursive=True)
+    if len(files) != 1:
+        raise ValueError(f"expected one *_{suffix}.csv under {d}, found {files}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def dispatches(rows):
+    """Dispatch_Id -> {name, start, end, counters} in dispatch order."""
+    out = {}
+    for r in rows:
+        d = out.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "start": int(r["Start_Timestamp"]),
+                                                   "end": int(r["End_Timestamp"]), "counters": {}})
+        if "Counter_Name" in r:
+            d["counters"][r["Counter_Name"]] = d["counters"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [out[k] for k in sorted(out)]
+
+
+def match(bench, disp, steps):
+    """bench name -> list (one entry per timed call) of lists of dispatches."""
+    kern = bench["kernels"]
+    step_names = [k for k, v in kern.items() if not v.get("outside_step")]
+    extra_names = [k for k, v in kern.items() if v.get("outside_step") and k != COPY]
+    fp8q = [d for d in disp if "fp8q::" in d["name"]]
+    # the warm-up count is not needed: step calls come first, so the number of
+    # step rounds is what remains after the outside-step calls
+    n_extra = sum(2 + steps for _ in extra_names)
+    calls = []          # consecutive calls, each a list of dispatches
+    i = 0
+    while i < len(fp8q):
+        c = [fp8q[i]]
+        i += 1
+        while i < len(fp8q) and is_second_grid(fp8q[i]["name"]) and "gemm" in c[0]["name"]:
+            c.append(fp8q[i])
+            i += 1
+        calls.append(c)
+    n_step_calls = len(calls) - n_extra
+    if n_step_calls <= 0 or n_step_calls % len(step_names):
+        raise ValueError(f"{len(calls)} calls do not split into step rounds of {len(step_names)} "
+                         f"plus {n_extra} outside-step calls")
+    rounds = n_step_calls // len(step_names)
+    if rounds < steps:
+        raise ValueError(f"only {rounds} step rounds for --steps {steps}")
+    seq = [n for _ in range(rounds) for n in step_names]
+    for n in extra_names:
+        seq += [n] * (2 + steps)
+    timed = {}
+    for pos, (n, c) in enumerate(zip(seq, calls)):
+        fam = family(n)
+        if fam not in c[0]["name"]:
+            raise ValueError(f"call {pos} ({n}) matched dispatch {c[0]['name'][:80]}")
+        timed.setdefault(n, []).append(c)
+    for n in timed:
+        timed[n] = timed[n][-steps:]
+    copies = [d for d in disp if "copy" in d["name"].lower()]
+    if copies:
+        big = max(d["end"] - d["start"] for d in copies)
+        timed[COPY] = [[d] for d in copies if d["end"] - d["start"] > big / 4][-5:]
+    return timed, list(kern)
+
+
+def dur_us(call):
+    return sum(d["end"] - d["start"] for d in call) / 1e3
+
+
+def cmd_trace(a):
+    bench = read_bench(a.bench)
+    disp = dispatches(read_csv(a.trace_dir, "kernel_trace"))
+    timed, order = match(bench, disp, a.steps)
+    stats = read_csv(a.trace_dir, "kernel_stats")
+    durs = {}
+    for d in disp:
+        durs.setdefault(d["name"], []).append((d["end"] - d["start"]) / 1e3)
+    print("| kernel | calls | avg us | median us | min us | max us | share |")
+    print("|---|---|---|---|---|---|---|")
+    for r in stats:
+        name = r["Name"] if len(r["Name"]) <= 110 else r["Name"][:107] + "..."
+        med = statistics.median(durs.get(r["Name"], [0.0]))
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {med:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    print()
+    print(f"Per bench call (mean over the {a.steps} timed calls; a call's grids summed), "
+          "beside the bench's own HIP-event time from its JSON line:")
+    print()
+    print("| bench kernel | grids per call | rocprofv3 us | HIP events us (bench line) |")
+    print("|---|---|---|---|")
+    for n in order:
+        if n not in timed:
+            continue
+        cs = timed[n]
+        us = statistics.mean(dur_us(c) for c in cs)
+        print(f"| {n} | {len(cs[0])} | {us:.1f} | {bench['kernels'][n]['us']:.1f} |")
+
+
+def compute_traffic(bench, fetch_rows, write_rows, clock_rows, steps, source_hash):
+    """hbm_traffic.json content from the three counter runs' counter_collection rows."""
+    runs = {}
+    for key, rows in (("FETCH_SIZE", fetch_rows), ("WRITE_SIZE", write_rows), ("clock", clock_rows)):
+        runs[key] = match(bench, dispatches(rows), steps)
+    order = runs["FETCH_SIZE"][1]
+    cal = {}
+    for key in ("FETCH_SIZE", "WRITE_SIZE"):
+        kib = statistics.median(c[0]["counters"][key] for c in runs[key][0][COPY])
+        cal[key] = {"copy_1GiB_counter_KiB": kib, "scale": (1 << 30) / (kib * 1024)}
+    per = {}
+    for key in ("FETCH_SIZE", "WRITE_SIZE"):
+        timed = runs[key][0]
+        per[key] = {n: statistics.mean(sum(d["counters"][key] for d in c) for c in timed[n]) * 1024
+                    * cal[key]["scale"] for n in order if n in timed and n != COPY}
+    clock = {}
+    for n, cs in runs["clock"][0].items():
+        if not n.startswith("gemm"):
+            continue
+        cyc = sum(d["counters"]["GRBM_GUI_ACTIVE"] for c in cs for d in c)
+        ns = sum(d["end"] - d["start"] for c in cs for d in c)
+        clock[n] = round(cyc / (XCDS * ns), 3)
+    cmd = "rocprofv3 --pmc {} -d <dir> --output-format csv -- python3 -u bench.py --steps %d --warmup 1 " \
+          "--no-cpu-baseline" % steps
+    return {
+        "source_hash": source_hash,
+        "command": cmd.format("FETCH_SIZE (then WRITE_SIZE)"),
+        "calibration": cal,
+        "fetch_bytes": per["FETCH_SIZE"],
+        "write_bytes": per["WRITE_SIZE"],
+        "kernels": {n: per["FETCH_SIZE"][n] + per["WRITE_SIZE"][n] for n in per["FETCH_SIZE"]},
+        "clock_command": cmd.format("GRBM_GUI_ACTIVE GRBM_COUNT"),
+        "clock_ghz": clock,
+    }
+
+
+def cmd_traffic(a):
+    sys.path.insert(0, ROOT)
+    from bench import source_hash
+    bench = read_bench(a.bench)
+    out = compute_traffic(bench, read_csv(a.fetch_dir, "counter_collection"),
+                          read_csv(a.write_dir, "counter_collection"), read_csv(a.clock_dir, "counter_collection"),
+                          a.steps, source_hash())
+    cal, clock = out["calibration"], out["clock_ghz"]
+    per = {"FETCH_SIZE": out["fetch_bytes"], "WRITE_SIZE": out["write_bytes"]}
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"Calibration on the 1 GiB device copy (1,073,741,824 bytes read and written): FETCH_SIZE reads "
+          f"{cal['FETCH_SIZE']['copy_1GiB_counter_KiB']:.1f} KiB (scale {cal['FETCH_SIZE']['scale']:.4f}), "
+          f"WRITE_SIZE reads {cal['WRITE_SIZE']['copy_1GiB_counter_KiB']:.1f} KiB "
+          f"(scale {cal['WRITE_SIZE']['scale']:.4f}).")
+    print()
+    print("| kernel (bench name) | fetched MB | written MB | total MB | algorithmic MB |")
+    print("|---|---|---|---|---|")
+    for n in per["FETCH_SIZE"]:
+        k = bench["kernels"][n]
+        alg = k.get("bytes")
+        alg_s = f"{alg / 1e6:.1f}" if alg else "-"
+        f, w = per["FETCH_SIZE"][n], per["WRITE_SIZE"][n]
+        print(f"| {n} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / 1e6:.1f} | {alg_s} |")
+    print()
+    print("| GEMM | average shader clock GHz |")
+    print("|---|---|")
+    for n, g in clock.items():
+        print(f"| {n} | {g:.2f} |")
+    print()
+    print(f"Kernel sources hash: `{out['source_hash']}`")
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = p.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("bench")
+    t.add_argument("trace_dir")
+    t.add_argument("--steps", type=int, required=True)
+    f = sub.add_parser("traffic")
+    f.add_argument("bench")
+    f.add_argument("fetch_dir")
+    f.add_argument("write_dir")
+    f.add_argument("clock_dir")
+    f.add_argument("--steps", type=int, required=True)
+    a = p.parse_args()
+    cmd_trace(a) if a.cmd == "trace" else cmd_traffic(a)
+
+
+if __name__ == "__main__":
+    main()

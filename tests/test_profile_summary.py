@@ -1,0 +1,90 @@
+"""Host logic of profile_summary.py: matching bench calls to rocprofv3 dispatches
+and calibrating the HBM counters (synthetic counter rows, no GPU)."""
+
+import os
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import profile_summary as ps  # noqa: E402
+
+DUAL = "void fp8q::quant_dual_kernel<unsigned short, 0>(unsigned short const*, long)"
+GEMM_A = "void fp8q::gemm_blockscaled_kernel<256, 256, 4, 2, 0, 0, false, 0>(fp8q::GemmArgs)"
+GEMM_B = "void fp8q::gemm_blockscaled_kernel<128, 256, 2, 4, 0, 0, false, 0>(fp8q::GemmArgs)"
+Q1 = "void fp8q::quant_1x128_kernel<unsigned short, 1>(unsigned short const*, long)"
+REDUCE = "void at::native::reduce_kernel<512, 1>(...)"
+COPY = "__amd_rocclr_copyBuffer"
+
+BENCH = {"kernels": {
+    "quant 1x128+128x1 X": {"us": 50.0},
+    "gemm Dgrad": {"us": 900.0},
+    "quant_1x128 X (pow2 scales)": {"us": 30.0, "outside_step": True},
+    ps.COPY: {"us": 400.0, "outside_step": True},
+}}
+
+
+def _rows(steps, warmup, counter):
+    """Dispatch rows as the bench would launch them; each call's counter value encodes
+    (kind, call index) so that the expected means are known."""
+    rows, t = [], 0
+    did = [0]
+
+    def add(name, value, dur=1000):
+        nonlocal t
+        did[0] += 1
+        rows.append({"Dispatch_Id": str(did[0]), "Kernel_Name": name, "Start_Timestamp": str(t),
+                     "End_Timestamp": str(t + dur), "Counter_Name": counter, "Counter_Value": str(value)})
+        t += dur + 10
+
+    add(COPY, 1.0, dur=5)                     # an early small copy (input upload)
+    for s in range(warmup + steps):
+        add(DUAL, 100 + s)
+        add(GEMM_A, 1000 + s, dur=8000)
+        add(GEMM_B, 10, dur=2000)             # second grid of the same Dgrad call
+    for c in range(2 + steps):
+        add(REDUCE, 0.0)                      # the cache scrub between timed calls
+        add(Q1, 50 + c)
+    for c in range(3 + 5):
+        add(COPY, 524288.0 if counter == "FETCH_SIZE" else 1048576.0, dur=400000)
+    return rows
+
+
+def test_match_pairs_split_grids_and_keeps_the_timed_calls():
+    steps, warmup = 2, 1
+    timed, order = ps.match(BENCH, ps.dispatches(_rows(steps, warmup, "FETCH_SIZE")), steps)
+    assert order == list(BENCH["kernels"])
+    assert [len(c) for c in timed["gemm Dgrad"]] == [2, 2]
+    assert [c[0]["counters"]["FETCH_SIZE"] for c in timed["gemm Dgrad"]] == [1001, 1002]
+    assert [c[0]["counters"]["FETCH_SIZE"] for c in timed["quant 1x128+128x1 X"]] == [101, 102]
+    assert [c[0]["counters"]["FETCH_SIZE"] for c in timed["quant_1x128 X (pow2 scales)"]] == [52, 53]
+    assert len(timed[ps.COPY]) == 5 and all(len(c) == 1 for c in timed[ps.COPY])
+
+
+def test_match_rejects_a_sequence_of_the_wrong_kind():
+    rows = _rows(2, 1, "FETCH_SIZE")
+    for r in rows:
+        if r["Kernel_Name"] == Q1:
+            r["Kernel_Name"] = DUAL
+    with pytest.raises(ValueError):
+        ps.match(BENCH, ps.dispatches(rows), 2)
+
+
+def test_traffic_is_calibrated_on_the_copy_and_sums_the_grids():
+    steps, warmup = 2, 1
+    fetch = _rows(steps, warmup, "FETCH_SIZE")
+    write = _rows(steps, warmup, "WRITE_SIZE")
+    clock = _rows(steps, warmup, "GRBM_GUI_ACTIVE")
+    out = ps.compute_traffic(BENCH, fetch, write, clock, steps, "hash")
+    # the copy moves 1 GiB each way; FETCH_SIZE read half of it -> scale 2
+    assert out["calibration"]["FETCH_SIZE"]["scale"] == pytest.approx(2.0)
+    assert out["calibration"]["WRITE_SIZE"]["scale"] == pytest.approx(1.0)
+    # Dgrad: mean of (1001 + 10) and (1002 + 10) KiB, times 1024 and the scale
+    assert out["fetch_bytes"]["gemm Dgrad"] == pytest.approx(1011.5 * 1024 * 2.0)
+    assert out["write_bytes"]["gemm Dgrad"] == pytest.approx(1011.5 * 1024 * 1.0)
+    assert out["kernels"]["gemm Dgrad"] == pytest.approx(1011.5 * 1024 * 3.0)
+    assert ps.COPY not in out["kernels"]
+    # clock: cycles over 8 XCDs x ns, both grids of both timed calls
+    assert out["clock_ghz"]["gemm Dgrad"] == pytest.approx(round((1001 + 10 + 1002 + 10) / (8 * 20000), 3))
+    assert set(out["clock_ghz"]) == {"gemm Dgrad"}
+    assert out["source_hash"] == "hash"
