@@ -133,10 +133,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   const int64_t tiles_m = p.M / BM;
   const int64_t tiles_n = p.N / BN;
   const int64_t ntiles = tiles_m * tiles_n;
-  // Workgroup i runs on XCD i % 8: give every XCD one contiguous range of
-  // tiles (ceil or floor of ntiles/8), so neighbouring tiles share its L2.
+  // Workgroup i runs on XCD i % 8.  Plain GEMMs: give every XCD one
+  // contiguous range of tiles (ceil or floor of ntiles/8), so neighbouring
+  // tiles share its L2.  Grouped GEMMs: deal the 32-tile runs of the
+  // grouped-M order (8 M-tiles x 4 N-tiles when N = 2048) to the XCDs in turn.
+  // A contiguous eighth of a grouped problem is one kind of group: with groups
+  // of very different sizes, one XCD got all the small groups, whose weight
+  // panels are read by one or two M-tiles each, and streamed them through its
+  // own link to memory while the XCDs of the largest group reused theirs from
+  // L2 (measured on 64 Zipf(1.1)-sized experts: 1120 -> 1076 us).  The runs
+  // keep each XCD's concurrent tiles on shared A and B panels.
   int64_t bid = blockIdx.x;
-  {
+  if constexpr (GROUPED) {
+    const int64_t full = (ntiles >> 8) << 8;    // whole rounds of 8 runs; the rest keep their order
+    if (bid < full) {
+      const int64_t x = bid & 7, l = bid >> 3;
+      bid = (((l >> 5) << 3) + x) * 32 + (l & 31);
+    }
+  } else {
     const int64_t q = ntiles >> 3, r = ntiles & 7, x = bid & 7, l = bid >> 3;
     bid = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + l;
   }

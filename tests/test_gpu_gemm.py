@@ -200,6 +200,28 @@ def test_grouped_tail_balanced_two_grid_launch(out):
         assert og.rel_frobenius(got[rows], want[rows]) <= tol, rows
 
 
+def test_grouped_runs_dealt_to_xcds_over_several_rounds():
+    """Six groups of very different sizes (64, 40, 24, 16, 10, 6 M-tiles) x N=2048: 640
+    tiles, i.e. a 512-tile first grid whose 32-tile runs go to the XCDs in turn over two
+    rounds, then the last 32 M-tiles as a second grid.  Every output is checked."""
+    fp8q = require_gpu()
+    rng = np.random.default_rng(95)
+    sizes = [64, 40, 24, 16, 10, 6]
+    g, n, k = len(sizes), 2048, 256
+    gmap = np.repeat(np.arange(g, dtype=np.int32), sizes)
+    tiles_m = gmap.size
+    ops = random_fp8_operands(96, 128 * tiles_m, n * g, k)
+    qa, sa = ops["qa"], ops["sa"]
+    qb = ops["qb"].reshape(g, n, k)
+    sb = np.exp2(rng.uniform(-8, -2, size=(g, n // 128, k // 128))).astype(np.float32)
+    ref = og.grouped_ref(qa, sa, qb, sb, gmap)
+    c = fp8q.fp8_gemm_blockscaled_grouped(dev(gmap), dev(qa), dev(sa), dev(qb), dev(sb))
+    got, want = host_bf16_as_f64(c), og.round_bf16(ref)
+    for t in range(tiles_m):                       # every 128-row tile, so a tile run twice or skipped shows
+        rows = slice(128 * t, 128 * (t + 1))
+        assert og.rel_frobenius(got[rows], want[rows]) <= TOL, t
+
+
 # ----------------------------------------------------------------------------
 # Full-size workloads: GPU quantizes and multiplies; the oracle quantizes the
 # sampled rows / bands itself from the same seeded inputs and recomputes the
