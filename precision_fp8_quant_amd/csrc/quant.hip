@@ -166,10 +166,16 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
   const int c8 = t & 7;
   const int q4 = t >> 3;
   const int64_t ctiles = (cols + 63) >> 6;
-  const int64_t tiles = ctiles * (rows >> 7);
+  const int64_t rtiles = rows >> 7;
+  const int64_t tiles = ctiles * rtiles;
+  // Column-major tile order: consecutive workgroups take consecutive row
+  // blocks of one 64-column strip, so together they write whole runs of each
+  // transposed output row (measured on the 8192x18432 gradient: 98.5 -> 87.0
+  // us against row-band order, whose neighbours write 128-byte pieces of
+  // different output rows).
   for (int64_t u = blockIdx.x; u < tiles; u += gridDim.x) {   // block-uniform: barriers stay matched
-  const int64_t col0 = (u % ctiles) * 64;
-  const int64_t rblk = u / ctiles;
+  const int64_t col0 = (u / rtiles) * 64;
+  const int64_t rblk = u % rtiles;
   const int64_t row0 = rblk * 128;
   const int64_t col = col0 + c8 * 8;
   const bool col_ok = col < cols;                 // cols % 8 == 0: all-or-nothing per thread
