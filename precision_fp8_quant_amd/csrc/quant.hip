@@ -244,6 +244,26 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kBPitch = 132;
 
+// Block (row, column) of work unit u for the kernels that write row-major and
+// transposed codes of 128x128 blocks: 2x2 groups of blocks in row-band order,
+// column-major inside a group, so both outputs leave in 256-byte runs of
+// neighbouring workgroups rather than one of them in 128-byte pieces.
+// Measured against row-band order: the 18432x7168 weight with its transposed
+// copy 93.0 -> 90.4 us, the one-pass 1x128 + 128x1 quantizer of the 8192x18432
+// gradient 113.7 -> 111.0 us (4x4 and 8x1 groups gained nothing).  Row-band
+// order where the block counts are odd.
+__device__ __forceinline__ void order_2x2(int64_t u, int64_t rblocks, int64_t cblocks, int64_t& br, int64_t& bc) {
+  if (((rblocks | cblocks) & 1) == 0) {
+    const int64_t grp = u >> 2, w = u & 3, gcols = cblocks >> 1;
+    br = (grp / gcols) * 2 + (w & 1);
+    bc = (grp % gcols) * 2 + (w >> 1);
+  } else {
+    br = u / cblocks;
+    bc = u % cblocks;
+  }
+}
+
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 8 : 4, 8)))
 void quant_128x128_kernel(
@@ -258,7 +278,9 @@ void quant_128x128_kernel(
   const int64_t cblocks = cols >> 7;
   const int64_t nblocks = cblocks * (rows >> 7);
   for (int64_t u = blockIdx.x; u < nblocks; u += gridDim.x) {   // block-uniform: barriers stay matched
-  const int64_t bc = u % cblocks, br = u / cblocks;
+  int64_t bc, br;                                 // block-uniform
+  if (q_t) order_2x2(u, rows >> 7, cblocks, br, bc);
+  else { bc = u % cblocks; br = u / cblocks; }   // row-major codes only: row-band order
   const int64_t col = bc * 128 + c16 * 8;
   const int64_t row_base = br * 128 + rq * 4;
   Raw8<T> v[4];                                   // [j]: row 4*rq + j, cols 8*c16..+7
@@ -402,7 +424,8 @@ void quant_dual_kernel(
   const int64_t cblocks = cols >> 7;
   const int64_t nblocks = cblocks * (rows >> 7);
   for (int64_t u = blockIdx.x; u < nblocks; u += gridDim.x) {   // block-uniform: barriers stay matched
-  const int64_t bc = u % cblocks, br = u / cblocks;   // row-band-major: concurrent workgroups share rows
+  int64_t bc, br;
+  order_2x2(u, rows >> 7, cblocks, br, bc);
   const int64_t col = bc * 128 + c16 * 8;
   const int64_t row_base = br * 128 + rq * 4;
   Raw8<T> v[4];                                   // [j]: row 4*rq + j, cols 8*c16..+7

@@ -220,6 +220,20 @@ def test_grouped_runs_dealt_to_xcds_over_several_rounds():
     for t in range(tiles_m):                       # every 128-row tile, so a tile run twice or skipped shows
         rows = slice(128 * t, 128 * (t + 1))
         assert og.rel_frobenius(got[rows], want[rows]) <= TOL, t
+    # out-of-range group ids scattered through the M-tiles: a workgroup walking
+    # several tiles skips those and goes on to its next tile; their rows stay untouched
+    gmap2 = gmap.copy()
+    gmap2[::7] = -1
+    gmap2[3] = g
+    c2 = torch.full((128 * tiles_m, n), 5.0, dtype=torch.float32, device="cuda")
+    fp8q.fp8_gemm_blockscaled_grouped(dev(gmap2), dev(qa), dev(sa), dev(qb), dev(sb), c=c2)
+    h2 = host(c2).astype(np.float64)
+    for t in range(tiles_m):
+        rows = slice(128 * t, 128 * (t + 1))
+        if gmap2[t] < 0 or gmap2[t] >= g:
+            assert np.all(h2[rows] == 5.0), t
+        else:
+            assert og.rel_frobenius(h2[rows], ref[rows]) <= TOL_F32, t
 
 
 # ----------------------------------------------------------------------------
