@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # kernel family expected for each bench name (checked on every matched dispatch)
 FAMILIES = [
-    ("requant", "requant_128x1_kernel"),
+    ("requant", "quant_128x1_kernel<unsigned char"),    # the 128x1 kernel reading FP8 codes
     ("quant 1x128+128x1", "quant_dual_kernel"),
     ("quant_128x128", "quant_128x128_kernel"),
     ("quant_1x128", "quant_1x128_kernel"),
