@@ -129,6 +129,21 @@ def test_one_pow2_operand_exact_small_integers(mask, kind):
     assert np.array_equal(got, ref), f"max abs diff {np.max(np.abs(got - ref))}"
 
 
+@pytest.mark.parametrize("mask", ["A", "B"])
+@pytest.mark.parametrize("kind", ["fprop", "wgrad"])
+def test_one_pow2_operand_accumulate(mask, kind):
+    """FP32 accumulate into an existing C with one operand's scales in the MFMA."""
+    fp8q = require_gpu()
+    m, n, k = 256, 512, 640
+    ops = _mixed_operands(231 + len(kind), m, n, k, kind, mask)
+    c0 = np.random.default_rng(232).standard_normal((m, n)).astype(np.float32)
+    c = dev(c0.copy())
+    fp8q.fp8_gemm_blockscaled_pow2(KINDS[kind], dev(ops["qa"]), dev(ops["sa"]), dev(ops["qb"]), dev(ops["sb"]), c=c,
+                                   accumulate=True, pow2_operands=MASKS[mask])
+    ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind) + c0.astype(np.float64)
+    assert og.rel_frobenius(host(c).astype(np.float64), ref) <= TOL
+
+
 def test_pow2_wgrad_accumulate_and_k_zero():
     fp8q = require_gpu()
     m, n, k = 256, 512, 384
