@@ -2,7 +2,8 @@
 //
 //  * 1x128 tiles (one token x 128 channels), scales [cols/128][rows]
 //  * 128x1 tiles (128 tokens x one channel), codes written transposed
-//  * 128x128 blocks (weights), optional transposed copy for Dgrad
+//  * 128x128 blocks (weights), optional transposed copy for Dgrad; without
+//    it, BF16 weights go two blocks per workgroup
 //  * 1x128 and 128x1 tiles of one tensor in one pass
 //  * FP8 -> FP8 re-tiling of 1x128 codes into 128x1 tiles (backward pass),
 //    by the 128x1 kernel reading codes and their row scales
@@ -11,7 +12,7 @@
 // excerpt, paragraphs 2 and 4; "Deepseek - Not For everyone", paragraph 3;
 // power-of-2 scales: dssusan.co.kr FP8 excerpt, paragraph 1.
 //
-// All four kernels are HBM-bound streaming passes: 16-byte coalesced loads,
+// All five kernels are HBM-bound streaming passes: 16-byte coalesced loads,
 // max-abs taken on the integer bit patterns of |x| (non-negative floats order
 // like their bits; BF16 pairs reduce two at a time with v_pk_max_u16),
 // reduced across lanes with DPP and the gfx950 permlane swaps (and LDS across
@@ -367,6 +368,74 @@ void quant_128x128_kernel(
   }
 }
 
+
+// BF16 128x128 blocks, row-major codes only, two horizontally adjacent blocks
+// per 512-thread workgroup (128 rows x 256 columns): thread t owns the 16
+// columns 16*(t%16)..+15 of rows 4*(t/16)..+3, so lanes 0-7 of a DPP row hold
+// the left block and lanes 8-15 the right one; each block's max goes over
+// its 8 lanes (quad permutes + row_half_mirror), across the wave's 4 DPP rows
+// with the permlane swaps and across the 8 waves through LDS.  Each thread
+// keeps two 16-byte loads per row in flight (64 VGPRs, still 8 waves per
+// SIMD), twice the one-block kernel's, and the codes leave as 512-byte row
+// pieces: measured on the 131072x7168 expert weights 527 -> 508 us.
+template <int MODE>
+__global__ __launch_bounds__(512) void quant_128x256_kernel(
+    const uint16_t* __restrict__ w, int64_t rows, int64_t cols, int64_t ld_w,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scales) {
+  __shared__ uint32_t wave_max[8][2];
+  const int t = threadIdx.x;
+  const int c16 = t & 15;
+  const int rq = t >> 4;
+  const int half = c16 >> 3;
+  const int64_t cpairs = cols >> 8;
+  const int64_t cblocks = cols >> 7;
+  const int64_t nunits = cpairs * (rows >> 7);
+  for (int64_t u = blockIdx.x; u < nunits; u += gridDim.x) {   // block-uniform: barriers stay matched
+  const int64_t bp = u % cpairs, br = u / cpairs;
+  const int64_t col = bp * 256 + c16 * 16;
+  const int64_t row_base = br * 128 + rq * 4;
+  Raw8<uint16_t> v[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j][0].load(w + (row_base + j) * ld_w + col);
+    v[j][1].load(w + (row_base + j) * ld_w + col + 8);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t b = v[j][h].amax_bits();
+      m = b > m ? b : m;
+    }
+  m = FP8Q_DPP_MAX(m, 0xB1);
+  m = FP8Q_DPP_MAX(m, 0x4E);
+  m = FP8Q_DPP_MAX(m, 0x141);                     // max over the 8 lanes of this block
+  {                                               // lanes l, l^16, l^32, l^48
+    const auto a = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    const uint32_t y = uint32_t(a[0]) > uint32_t(a[1]) ? uint32_t(a[0]) : uint32_t(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(y, y, false, false);
+    m = uint32_t(b[0]) > uint32_t(b[1]) ? uint32_t(b[0]) : uint32_t(b[1]);
+  }
+  if ((t & 55) == 0) wave_max[t >> 6][(t >> 3) & 1] = m;   // lanes 0 and 8 of each wave
+  __syncthreads();
+  m = wave_max[0][half];
+#pragma unroll
+  for (int p = 1; p < 8; ++p) m = wave_max[p][half] > m ? wave_max[p][half] : m;
+  const ScalePair sp = scale_from_amax_bits<MODE>(m);
+  if (t == 0 || t == 8) scales[br * cblocks + bp * 2 + half] = sp.s;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 out = {cvt4<MODE>(v[j][0].get(0), v[j][0].get(1), v[j][0].get(2), v[j][0].get(3), sp.inv),
+                       cvt4<MODE>(v[j][0].get(4), v[j][0].get(5), v[j][0].get(6), v[j][0].get(7), sp.inv),
+                       cvt4<MODE>(v[j][1].get(0), v[j][1].get(1), v[j][1].get(2), v[j][1].get(3), sp.inv),
+                       cvt4<MODE>(v[j][1].get(4), v[j][1].get(5), v[j][1].get(6), v[j][1].get(7), sp.inv)};
+    *reinterpret_cast<u32x4*>(q + (row_base + j) * ld_q + col) = out;
+  }
+  __syncthreads();                                // wave_max is reused by the next unit
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Both tilings of one tensor in one pass (dssusan.co.kr FP8 excerpt,
 // paragraph 4: the backward pass needs the output gradient in 1x128 tiles for
@@ -566,6 +635,16 @@ hipError_t launch_quant_128x1(const void* x_, bool bf16, int64_t rows, int64_t c
 hipError_t launch_quant_128x128(const void* x_, bool bf16, int64_t rows, int64_t cols, int64_t ld_w,
                                 int mode, uint8_t* q, int64_t ld_q, float* scales,
                                 uint8_t* q_t, int64_t ld_qt, float* scales_t, hipStream_t st) {
+  if (bf16 && q_t == nullptr && cols % 256 == 0) {
+    const dim3 grid2(unit_grid((cols / 256) * (rows / 128)));
+    const uint16_t* w = static_cast<const uint16_t*>(x_);
+    if (mode == kModePow2)
+      hipLaunchKernelGGL((quant_128x256_kernel<kModePow2>), grid2, dim3(512), 0, st, w, rows, cols, ld_w, q, ld_q, scales);
+    else
+      hipLaunchKernelGGL((quant_128x256_kernel<kModeMaxAbs>), grid2, dim3(512), 0, st, w, rows, cols, ld_w, q, ld_q,
+                         scales);
+    return hipGetLastError();
+  }
   const dim3 grid(unit_grid((cols / 128) * (rows / 128)));
   FP8Q_DISPATCH_T(quant_128x128_kernel, 512, bf16, mode, grid, st, rows, cols, ld_w, q, ld_q, scales, q_t, ld_qt,
                 scales_t);

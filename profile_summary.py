@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 FAMILIES = [
     ("requant", "quant_128x1_kernel<unsigned char"),    # the 128x1 kernel reading FP8 codes
     ("quant 1x128+128x1", "quant_dual_kernel"),
-    ("quant_128x128", "quant_128x128_kernel"),
+    ("quant_128x128", ("quant_128x128_kernel", "quant_128x256_kernel")),   # one- or two-block workgroups
     ("quant_1x128", "quant_1x128_kernel"),
     ("quant_128x1", "quant_128x1_kernel"),
     ("gemm", "gemm_blockscaled_kernel"),
@@ -42,9 +42,10 @@ XCDS = 8
 
 
 def family(bench_name):
+    """Kernel names (a tuple) that a bench call of this name may launch."""
     for prefix, fam in FAMILIES:
         if bench_name.startswith(prefix):
-            return fam
+            return fam if isinstance(fam, tuple) else (fam,)
     raise ValueError(f"no kernel family for bench name {bench_name!r}")
 
 
@@ -111,8 +112,7 @@ def match(bench, disp, steps):
         seq += [n] * (2 + steps)
     timed = {}
     for pos, (n, c) in enumerate(zip(seq, calls)):
-        fam = family(n)
-        if fam not in c[0]["name"]:
+        if not any(f in c[0]["name"] for f in family(n)):
             raise ValueError(f"call {pos} ({n}) matched dispatch {c[0]['name'][:80]}")
         timed.setdefault(n, []).append(c)
     for n in timed:

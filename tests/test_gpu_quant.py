@@ -122,7 +122,7 @@ def test_quant_128x1(dtype, mode_name, mode, shape):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mode_name,mode", MODES)
-@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 256)])
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 256), (256, 1024)])
 def test_quant_block(dtype, mode_name, mode, shape):
     fp8q = require_gpu()
     x_dev, x_ref = _to_dev(_data(11 + shape[0], shape, sigma=0.02), dtype)
