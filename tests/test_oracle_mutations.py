@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import e4m3, gemm, quant
+import tests.test_oracle_bf16 as pins_bf16
 import tests.test_oracle_e4m3 as pins_e4m3
 import tests.test_oracle_gemm as pins_gemm
 import tests.test_oracle_quant as pins_quant
@@ -99,3 +100,21 @@ def test_requant_with_another_groups_scale_is_caught(monkeypatch):
     monkeypatch.setattr(quant, "requant_1x128_to_128x1", _requant_wrong_group_scale)
     with pytest.raises(AssertionError):
         pins_quant.test_requant_error_bound_against_source(quant.MODE_POW2)
+
+
+def _widen_shift_15(bits):
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(15)).view(np.float32)
+
+
+def _widen_without_shift(bits):
+    # the pattern left in the low half of the float32 word
+    return np.asarray(bits, dtype=np.uint16).astype(np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("mutant", [_widen_shift_15, _widen_without_shift], ids=["shift15", "no-shift"])
+def test_wrong_bf16_widening_is_caught(mutant):
+    with pytest.raises(AssertionError):
+        pins_bf16.test_every_pattern_matches_torch_cast(mutant)
+    with pytest.raises(AssertionError):
+        pins_bf16.test_field_layout_values(mutant)

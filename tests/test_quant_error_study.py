@@ -62,3 +62,21 @@ def test_delayed_scaling_clips_an_unseen_spike():
     assert clipped[4] > 0 and all(c == 0 for i, c in enumerate(clipped) if i != 4)
     assert errs[4] > 10 * online
     assert max(errs[:4] + errs[5:]) <= 2.0 ** -4
+
+
+def test_underflow_fraction_closed_form():
+    # nonzero inputs whose code is +0 (0x00) or -0 (0x80) over all nonzero inputs;
+    # zero inputs do not count, whatever their code
+    x = np.array([1.0, -1.0, 2.0, 3.0, 0.0, 0.0, -5.0, 7.0], np.float32)
+    q = np.array([0x00, 0x80, 0x01, 0x7E, 0x00, 0x80, 0x81, 0xFE], np.uint8)
+    assert study.underflow_fraction(q, x) == 2 / 6
+    assert study.underflow_fraction(np.array([0x08, 0x88], np.uint8), np.array([1.0, -1.0], np.float32)) == 0.0
+    assert study.underflow_fraction(np.array([0x80], np.uint8), np.array([-1e-30], np.float32)) == 1.0
+
+
+def test_underflow_fraction_counts_values_below_half_the_smallest_subnormal():
+    # with unit scales, |x| <= 2^-10 (half of E4M3's smallest subnormal 2^-9) rounds to zero
+    # (the tie 2^-10 goes to the even code 0); 2^-9 and above does not
+    x = np.array([2.0 ** -11, -(2.0 ** -10), 2.0 ** -9, 1.0], np.float32)
+    q, _ = study.quant_with_scale(x, np.float32(1.0), np.float32(1.0))
+    assert study.underflow_fraction(q, x) == 2 / 4
