@@ -107,7 +107,9 @@ int fp8_quant_tile(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
  * scales   : scales[rows/128][cols/128], packed.
  * q_t      : optional (NULL to skip): the transposed codes q_t[cols][rows],
  *            leading dimension ld_qt (bytes); q_t[c*ld_qt + r] == q[r*ld_q + c].
- * scales_t : required iff q_t is given: scales_t[cols/128][rows/128] == scales^T.
+ * scales_t : required iff q_t is given: scales_t[cols/128][rows/128] == scales^T
+ *            (q_t without scales_t: FP8Q_ERR_NULL; scales_t without q_t:
+ *            FP8Q_ERR_ARG).
  *            The transposed pair is the K-contiguous weight operand of Dgrad.
  * Requires rows % 128 == 0 and cols % 128 == 0.
  */

@@ -193,6 +193,8 @@ def fp8_quant_block(w, mode=MAXABS, transposed=False, q=None, scales=None, q_t=N
     _rowmajor(w, "w")
     rows, cols = w.shape
     dev = w.device
+    if not transposed and (q_t is not None or scales_t is not None):
+        raise ValueError("q_t / scales_t are the transposed copy: pass transposed=True")
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if scales is None:

@@ -15,16 +15,31 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Range {
   uintptr_t lo, hi;   // [lo, hi)
+  bool ok;            // false: the extent overflows 64 bits or the address space
 };
 
-// Bytes spanned by a row-major matrix with `rows` rows of `cols` elements.
+// Bytes spanned by a row-major matrix with `rows` rows of `cols` elements,
+// ((rows - 1) * ld + cols) * esize, with every step checked for overflow
+// (the sizes are non-negative here: negative ones were rejected before).
 Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  if (rows <= 0 || cols <= 0) return {lo, lo};
-  return {lo, lo + uintptr_t(((rows - 1) * ld + cols) * esize)};
+  if (rows <= 0 || cols <= 0) return {lo, lo, true};
+  int64_t elems = 0, bytes = 0;
+  uintptr_t hi = 0;
+  if (__builtin_mul_overflow(rows - 1, ld, &elems) || __builtin_add_overflow(elems, cols, &elems) ||
+      __builtin_mul_overflow(elems, esize, &bytes) || __builtin_add_overflow(lo, uintptr_t(bytes), &hi))
+    return {lo, lo, false};
+  return {lo, hi, true};
 }
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// a * b for non-negative a, b; false on overflow
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+// A leading dimension of `ld` elements of `esize` (2 or 4) bytes is a multiple
+// of 16 bytes (without forming ld * esize, which could overflow).
+bool ld16(int64_t ld, int64_t esize) { return ld % (16 / esize) == 0; }
 
 int64_t dtype_size(int dt) { return dt == FP8Q_BF16 ? 2 : 4; }
 bool dtype_ok(int dt) { return dt == FP8Q_BF16 || dt == FP8Q_F32; }
@@ -48,18 +63,22 @@ int check_gemm(int kind, int64_t M, int64_t N, int64_t K, const uint8_t* a, int6
   if (K > 0 && (!a || !b || !a_scales || !b_scales)) return FP8Q_ERR_NULL;
   if (ldc < N || (K > 0 && (lda < K || ldb < K))) return FP8Q_ERR_SHAPE;
   const int64_t es = dtype_size(c_dtype);
-  if (!aligned16(c) || (ldc * es) % 16) return FP8Q_ERR_ALIGN;
+  if (!aligned16(c) || !ld16(ldc, es)) return FP8Q_ERR_ALIGN;
   if (K > 0 && (!aligned16(a) || !aligned16(b) || !aligned16(a_scales) || !aligned16(b_scales) ||
                 lda % 16 || ldb % 16))
     return FP8Q_ERR_ALIGN;
   if (M % 128 || N % 128 || K % 128) return FP8Q_ERR_UNSUPPORTED;
   if (accumulate && c_dtype != FP8Q_F32) return FP8Q_ERR_UNSUPPORTED;
-  if ((M / 128) * (N / 128) > kMaxGridX) return FP8Q_ERR_UNSUPPORTED;
-  const int64_t nsa = (K / 128) * M;
-  const int64_t nsb = kind == FP8Q_WGRAD ? (K / 128) * N : (N / 128) * (K / 128);
+  if (N / 128 > kMaxGridX / (M / 128)) return FP8Q_ERR_UNSUPPORTED;   // tiles beyond one grid
+  int64_t nsa = 0, nsb = 0;
+  if (!mul_ok(K / 128, M, &nsa) || !mul_ok(K / 128, N, &nsb)) return FP8Q_ERR_SHAPE;
+  if (kind != FP8Q_WGRAD) nsb = (N / 128) * (K / 128);
   const Range rc = span(c, M, N, ldc, es);
   const Range ins[4] = {span(a, M, K, lda, 1), span(b, N, K, ldb, 1),
                         span(a_scales, 1, nsa, nsa, 4), span(b_scales, 1, nsb, nsb, 4)};
+  if (!rc.ok) return FP8Q_ERR_SHAPE;
+  for (int i = 0; i < 4; ++i)
+    if (!ins[i].ok) return FP8Q_ERR_SHAPE;
   for (int i = 0; i < 4; ++i)
     if (overlap(rc, ins[i])) return FP8Q_ERR_ALIAS;
   return FP8Q_OK;
@@ -97,18 +116,19 @@ int fp8_quant_tile(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
   if (ld_x < cols) return FP8Q_ERR_SHAPE;
   const bool t1x128 = tile == FP8Q_TILE_1x128;
   if (ld_q < (t1x128 ? cols : rows)) return FP8Q_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || (ld_x * es) % 16 || ld_q % 16)
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || !ld16(ld_x, es) || ld_q % 16)
     return FP8Q_ERR_ALIGN;
   if (t1x128) {
     if (cols % 128) return FP8Q_ERR_UNSUPPORTED;
   } else {
     if (rows % 128 || cols % 8) return FP8Q_ERR_UNSUPPORTED;
-
   }
+  int64_t nscale = 0;
+  if (!(t1x128 ? mul_ok(cols / 128, rows, &nscale) : mul_ok(rows / 128, cols, &nscale))) return FP8Q_ERR_SHAPE;
   const Range rx = span(x, rows, cols, ld_x, es);
   const Range rq = t1x128 ? span(q, rows, cols, ld_q, 1) : span(q, cols, rows, ld_q, 1);
-  const int64_t nscale = t1x128 ? (cols / 128) * rows : (rows / 128) * cols;
   const Range rs = span(scales, 1, nscale, nscale, 4);
+  if (!rx.ok || !rq.ok || !rs.ok) return FP8Q_ERR_SHAPE;
   if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs)) return FP8Q_ERR_ALIAS;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool bf16 = x_dtype == FP8Q_BF16;
@@ -125,21 +145,25 @@ int fp8_quant_block(const void* w, int w_dtype, int64_t rows, int64_t cols, int6
   if (rows == 0 || cols == 0) return FP8Q_OK;
   if (!w || !q || !scales) return FP8Q_ERR_NULL;
   if (q_t && !scales_t) return FP8Q_ERR_NULL;
+  if (scales_t && !q_t) return FP8Q_ERR_ARG;         // the transposed pair comes together
   const int64_t es = dtype_size(w_dtype);
   if (ld_w < cols || ld_q < cols || (q_t && ld_qt < rows)) return FP8Q_ERR_SHAPE;
-  if (!aligned16(w) || !aligned16(q) || !aligned16(scales) || (ld_w * es) % 16 || ld_q % 16)
+  if (!aligned16(w) || !aligned16(q) || !aligned16(scales) || !ld16(ld_w, es) || ld_q % 16)
     return FP8Q_ERR_ALIGN;
   if (q_t && (!aligned16(q_t) || !aligned16(scales_t) || ld_qt % 16)) return FP8Q_ERR_ALIGN;
-  if (scales_t && !aligned16(scales_t)) return FP8Q_ERR_ALIGN;
   if (rows % 128 || cols % 128) return FP8Q_ERR_UNSUPPORTED;
 
-  const int64_t nscale = (rows / 128) * (cols / 128);
+  int64_t nscale = 0;
+  if (!mul_ok(rows / 128, cols / 128, &nscale)) return FP8Q_ERR_SHAPE;
   const Range rw = span(w, rows, cols, ld_w, es);
   const Range rq = span(q, rows, cols, ld_q, 1);
   const Range rs = span(scales, 1, nscale, nscale, 4);
-  const Range rqt = q_t ? span(q_t, cols, rows, ld_qt, 1) : Range{0, 0};
-  const Range rst = scales_t ? span(scales_t, 1, nscale, nscale, 4) : Range{0, 0};
+  const Range rqt = q_t ? span(q_t, cols, rows, ld_qt, 1) : Range{0, 0, true};
+  const Range rst = scales_t ? span(scales_t, 1, nscale, nscale, 4) : Range{0, 0, true};
   const Range outs[4] = {rq, rs, rqt, rst};
+  if (!rw.ok) return FP8Q_ERR_SHAPE;
+  for (int i = 0; i < 4; ++i)
+    if (!outs[i].ok) return FP8Q_ERR_SHAPE;
   for (int i = 0; i < 4; ++i) {
     if (overlap(rw, outs[i])) return FP8Q_ERR_ALIAS;
     for (int j = i + 1; j < 4; ++j)
@@ -161,13 +185,17 @@ int fp8_quant_tile_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, 
   const int64_t es = dtype_size(x_dtype);
   if (ld_x < cols || ld_q < cols || ld_qt < rows) return FP8Q_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || !aligned16(q_t) || !aligned16(scales_t) ||
-      (ld_x * es) % 16 || ld_q % 16 || ld_qt % 16)
+      !ld16(ld_x, es) || ld_q % 16 || ld_qt % 16)
     return FP8Q_ERR_ALIGN;
   if (rows % 128 || cols % 128) return FP8Q_ERR_UNSUPPORTED;
-  const int64_t n1 = (cols / 128) * rows, n2 = (rows / 128) * cols;
+  int64_t n1 = 0, n2 = 0;
+  if (!mul_ok(cols / 128, rows, &n1) || !mul_ok(rows / 128, cols, &n2)) return FP8Q_ERR_SHAPE;
   const Range rx = span(x, rows, cols, ld_x, es);
   const Range outs[4] = {span(q, rows, cols, ld_q, 1), span(scales, 1, n1, n1, 4),
                          span(q_t, cols, rows, ld_qt, 1), span(scales_t, 1, n2, n2, 4)};
+  if (!rx.ok) return FP8Q_ERR_SHAPE;
+  for (int i = 0; i < 4; ++i)
+    if (!outs[i].ok) return FP8Q_ERR_SHAPE;
   for (int i = 0; i < 4; ++i) {
     if (overlap(rx, outs[i])) return FP8Q_ERR_ALIAS;
     for (int j = i + 1; j < 4; ++j)
@@ -189,9 +217,11 @@ int fp8_requant_1x128_to_128x1(const uint8_t* q, int64_t rows, int64_t cols, int
       ld_qt % 16)
     return FP8Q_ERR_ALIGN;
   if (rows % 128 || cols % 128) return FP8Q_ERR_UNSUPPORTED;
-  const int64_t nscale = (rows / 128) * cols;   // same count on both sides
+  int64_t nscale = 0;                           // same count on both sides
+  if (!mul_ok(rows / 128, cols, &nscale)) return FP8Q_ERR_SHAPE;
   const Range ins[2] = {span(q, rows, cols, ld_q, 1), span(scales, 1, nscale, nscale, 4)};
   const Range outs[2] = {span(q_t, cols, rows, ld_qt, 1), span(scales_t, 1, nscale, nscale, 4)};
+  if (!ins[0].ok || !ins[1].ok || !outs[0].ok || !outs[1].ok) return FP8Q_ERR_SHAPE;
   if (overlap(outs[0], outs[1])) return FP8Q_ERR_ALIAS;
   for (int i = 0; i < 2; ++i)
     for (int j = 0; j < 2; ++j)
@@ -244,18 +274,23 @@ int fp8_gemm_blockscaled_grouped(int32_t num_groups, int64_t M_total, int64_t N,
   if (K > 0 && (!a || !b || !a_scales || !b_scales)) return FP8Q_ERR_NULL;
   if (ldc < N || (K > 0 && lda < K)) return FP8Q_ERR_SHAPE;
   const int64_t es = dtype_size(c_dtype);
-  if (!aligned16(c) || (reinterpret_cast<uintptr_t>(group_of_mtile) & 3u) || (ldc * es) % 16)
+  if (!aligned16(c) || (reinterpret_cast<uintptr_t>(group_of_mtile) & 3u) || !ld16(ldc, es))
     return FP8Q_ERR_ALIGN;
   if (K > 0 && (!aligned16(a) || !aligned16(b) || !aligned16(a_scales) || !aligned16(b_scales) || lda % 16))
     return FP8Q_ERR_ALIGN;
   if (M_total % 128 || N % 128 || K % 128) return FP8Q_ERR_UNSUPPORTED;
-  if ((M_total / 128) * (N / 128) > kMaxGridX) return FP8Q_ERR_UNSUPPORTED;
-  const int64_t nsa = (K / 128) * M_total;
-  const int64_t nsb = int64_t(num_groups) * (N / 128) * (K / 128);
+  if (N / 128 > kMaxGridX / (M_total / 128)) return FP8Q_ERR_UNSUPPORTED;   // tiles beyond one grid
+  int64_t nsa = 0, nsb = 0, brows = 0;
+  if (!mul_ok(K / 128, M_total, &nsa) || !mul_ok(N / 128, K / 128, &nsb) ||
+      !mul_ok(int64_t(num_groups), nsb, &nsb) || !mul_ok(int64_t(num_groups), N, &brows))
+    return FP8Q_ERR_SHAPE;
   const Range rc = span(c, M_total, N, ldc, es);
-  const Range ins[5] = {span(a, M_total, K, lda, 1), span(b, int64_t(num_groups) * N, K, K, 1),
+  const Range ins[5] = {span(a, M_total, K, lda, 1), span(b, brows, K, K, 1),
                         span(a_scales, 1, nsa, nsa, 4), span(b_scales, 1, nsb, nsb, 4),
                         span(group_of_mtile, 1, M_total / 128, M_total / 128, 4)};
+  if (!rc.ok) return FP8Q_ERR_SHAPE;
+  for (int i = 0; i < 5; ++i)
+    if (!ins[i].ok) return FP8Q_ERR_SHAPE;
   for (int i = 0; i < 5; ++i)
     if (overlap(rc, ins[i])) return FP8Q_ERR_ALIAS;
   return from_hip(fp8q::launch_gemm_grouped(num_groups, M_total, N, K, group_of_mtile, a, lda, a_scales,

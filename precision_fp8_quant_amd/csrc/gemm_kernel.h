@@ -120,7 +120,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   static_assert(A_DMA * 1024 * NW == A_BYTES && B_DMA * 1024 * NW == B_BYTES, "DMA split");
   static_assert(BSCALE != kScaleRow || BN <= 256, "row scales: one DMA of at most 64 lanes x 4 floats");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + SB_SLOTS * SB_BYTES];
+  // K-group stages (and Wgrad's per-column B scales), reused by the epilogue
+  // to stage the output tile (TM rows of 64 columns per wave, padded rows)
+  constexpr int LOOP_LDS = 2 * STAGE + SB_SLOTS * SB_BYTES;
+  constexpr int EPI_LDS = NW * TM * (64 * (OUT == kOutBF16 ? 2 : 4) + 16);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LOOP_LDS > EPI_LDS ? LOOP_LDS : EPI_LDS];
   uint8_t* const sb_ring = smem + 2 * STAGE;
 
   const int tid = threadIdx.x;
@@ -374,8 +378,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
           if constexpr (BSCALE == kScaleRow && !B_HW && A_HW) {
             acc[mu][pn][js][j] = __builtin_fmaf(d[j], sbq[bu % 3][j], acc[mu][pn][js][j]);
           } else {
-            const float dj = (BSCALE == kScaleRow && !B_HW) ? d[j] * sbq[bu % 3][j] : d[j];
-            acc[mu][pn][js][j] = __builtin_fmaf(dj, cs[mu], acc[mu][pn][js][j]);
+            // the combined scale sa*sb first, then one fused multiply-add of
+            // the partial: no intermediate depends on the partial's size
+            const float cj = (BSCALE == kScaleRow && !B_HW) ? cs[mu] * sbq[bu % 3][j] : cs[mu];
+            acc[mu][pn][js][j] = __builtin_fmaf(d[j], cj, acc[mu][pn][js][j]);
           }
         }
       }
@@ -398,13 +404,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
           for (int d = 0; d < 4; ++d) acc[a][b][c][d] = accv[a][b][c][d];
   }
 
-  // ---- epilogue: each lane writes 16 consecutive columns of SM*PN rows ----
+  // ---- epilogue ----------------------------------------------------------
+  // A lane holds 16 consecutive columns of one row per (ms, pn).  Stored as
+  // they are, one store instruction wrote 16-byte pieces of 32 (BF16) or 64
+  // (FP32) different 128-byte lines, and writing the output was the costliest
+  // part of a tile (measured on the bench shapes: full-line stores made Fprop
+  // 6% and, non-temporal, the FP32 Wgrad 9% faster).  So the tile leaves
+  // through LDS, which the last K-group's barrier has freed: each wave writes
+  // one 64-column panel at a time into its own region (rows padded by 16
+  // bytes, which keeps both the writes and the read-back free of bank
+  // conflicts) and reads it back so that 8 lanes hold one whole line; every
+  // store instruction then writes whole lines of 8 (BF16) or 4 (FP32) rows.
+  // A wave's LDS instructions run in order, so it reuses its region for the
+  // next panel without a wait.  Non-temporal stores: the output goes to HBM
+  // while the GEMM, which is MFMA-bound, still runs, instead of lingering
+  // dirty in the memory-side cache for the next kernel to write back
+  // (measured: the 1x128 + 128x1 quantizer of an 8192x18432 gradient after
+  // Fprop, 126 -> 113 us).
+  constexpr int ESZ = OUT == kOutBF16 ? 2 : 4;
+  constexpr int PITCH = 64 * ESZ + 16;                  // bytes per staged row
+  constexpr int LPR = 64 * ESZ / 16;                     // lanes per 64-column row: 8 or 16
+  constexpr int RPI = 64 / LPR;                          // rows per store instruction: 8 or 4
+  static_assert(NW * TM * PITCH <= int(sizeof(smem)), "epilogue staging fits the LDS");
+  uint8_t* const stg = smem + wave * (TM * PITCH);
 #pragma unroll
-  for (int ms = 0; ms < SM; ++ms) {
-    const int64_t m = m_lane + 16 * ms;
+  for (int pn = 0; pn < PN; ++pn) {
 #pragma unroll
-    for (int pn = 0; pn < PN; ++pn) {
-      const int64_t n = n_wave + 64 * pn + 16 * lq;
+    for (int ms = 0; ms < SM; ++ms) {
+      uint8_t* row = stg + (16 * ms + lr) * PITCH;
       if constexpr (OUT == kOutBF16) {
         uint32_t w[8];
 #pragma unroll
@@ -412,24 +439,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
           w[2 * js] = bf16_rne_bits(acc[ms][pn][js][0]) | (bf16_rne_bits(acc[ms][pn][js][1]) << 16);
           w[2 * js + 1] = bf16_rne_bits(acc[ms][pn][js][2]) | (bf16_rne_bits(acc[ms][pn][js][3]) << 16);
         }
-        // Non-temporal stores: the BF16 output goes to HBM while the GEMM,
-        // which is MFMA-bound, still runs, instead of lingering dirty in the
-        // memory-side cache until the next (HBM-bound) kernel evicts it and
-        // pays for the write-back (measured: the 1x128 + 128x1 quantizer of a
-        // 8192x18432 gradient after Fprop, 126 -> 113 us; the GEMMs unchanged).
-        // The FP32 outputs keep ordinary stores: non-temporal ones slowed the
-        // 18432x7168 FP32 Wgrad by 6%.
-        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + m * p.ldc + n);
-        __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, dst);
-        __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, dst + 1);
+        *reinterpret_cast<u32x4*>(row + 32 * lq) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(row + 32 * lq + 16) = u32x4{w[4], w[5], w[6], w[7]};
+      } else {
+#pragma unroll
+        for (int js = 0; js < 4; ++js)
+          *reinterpret_cast<v4f*>(row + 64 * lq + 16 * js) =
+              v4f{acc[ms][pn][js][0], acc[ms][pn][js][1], acc[ms][pn][js][2], acc[ms][pn][js][3]};
+      }
+    }
+    const int chunk = lane % LPR;
+#pragma unroll
+    for (int sr = 0; sr < TM / RPI; ++sr) {
+      const int r = sr * RPI + lane / LPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * PITCH + 16 * chunk);
+      const int64_t m = m0 + wm * TM + r;
+      const int64_t n = n_wave + 64 * pn + chunk * (16 / ESZ);
+      if constexpr (OUT == kOutBF16) {
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + m * p.ldc + n));
       } else {
         v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.c) + m * p.ldc + n);
-#pragma unroll
-        for (int js = 0; js < 4; ++js) {
-          v4f o = {acc[ms][pn][js][0], acc[ms][pn][js][1], acc[ms][pn][js][2], acc[ms][pn][js][3]};
-          if constexpr (OUT == kOutF32Acc) o += dst[js];
-          dst[js] = o;
-        }
+        v4f o = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+        if constexpr (OUT == kOutF32Acc) o += *dst;
+        __builtin_nontemporal_store(o, dst);
       }
     }
   }

@@ -84,6 +84,7 @@ def test_quant_block_validation():
     assert _block(mode=9) == fp8q.ERR_ARG
     assert _block(q=None) == fp8q.ERR_NULL
     assert _block(qt=D, ldqt=256) == fp8q.ERR_NULL             # q_t without scales_t
+    assert _block(st=D) == fp8q.ERR_ARG                         # scales_t without q_t
     assert _block(qt=D, ldqt=128, st=D + 0x100000) == fp8q.ERR_SHAPE
     assert _block(rows=200) == fp8q.ERR_UNSUPPORTED
     assert _block(ldq=392) == fp8q.ERR_ALIGN

@@ -99,6 +99,81 @@ def test_tail_balanced_two_grid_launch(kind, out):
         assert og.rel_frobenius(got[:, cols], want[:, cols]) <= tol, cols
 
 
+@pytest.mark.parametrize("kind,out,k", [("wgrad", "f32", 384), ("wgrad", "f32acc", 1024),
+                                         ("fprop", "f32", 1024), ("fprop", "f32acc", 384)])
+def test_many_tile_fp32_launch_every_tile(kind, out, k):
+    """FP32 outputs over 16x32 = 512 tiles of 256x256 (two full waves on 256
+    CUs), plain and accumulating: every output tile is checked on its own (the
+    epilogue stages each wave's panels through LDS and writes whole lines), and
+    the result is deterministic."""
+    fp8q = require_gpu()
+    m, n = 4096, 8192
+    ops = random_fp8_operands(301 + k, m, n, k, kind=kind)
+    ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind)
+    args = [dev(ops[x]) for x in ("qa", "sa", "qb", "sb")]
+    c0 = np.random.default_rng(302).standard_normal((m, n)).astype(np.float32)
+    outs = []
+    for _ in range(2):
+        if out == "f32":
+            c = fp8q.fp8_gemm_blockscaled(KINDS[kind], *args, out_dtype=torch.float32)
+            want = og.round_output(ref, "f32")
+        else:
+            c = dev(c0.copy())
+            fp8q.fp8_gemm_blockscaled(KINDS[kind], *args, c=c, accumulate=True)
+            want = ref + c0.astype(np.float64)
+        outs.append(host(c))
+    got = outs[0].astype(np.float64)
+    assert np.array_equal(outs[0], outs[1])
+    # every 256x256 tile on its own (a split tile's two parts must both land)
+    for r in range(0, m, 256):
+        for cc in range(0, n, 256):
+            t = (slice(r, r + 256), slice(cc, cc + 256))
+            assert og.rel_frobenius(got[t], want[t]) <= TOL_F32, (r, cc)
+
+
+def _scale_pairs(rng, kind, m, n, k, lo, hi, spread):
+    """Non-power-of-two scales whose per-group products sa*sb lie in [2^lo, 2^hi]
+    while each scale on its own ranges over up to 2^+-spread: group g draws a
+    product exponent p_g (evenly spaced over [lo, hi - 4]) and a base exponent e_g;
+    A scales are 2^(e_g + u), B scales 2^(p_g - e_g + v), u and v uniform in
+    [0, 2).  e_g is drawn where both scales stay FP32 normal numbers below 2^126."""
+    g = k // 128
+    pr = np.linspace(lo, hi - 4, g)
+    e_lo = np.maximum(np.maximum(-spread, pr - 124), -126)
+    e_hi = np.minimum(np.minimum(spread, pr + 126), 124)
+    e = rng.uniform(e_lo, e_hi)
+    sa = np.exp2(e[:, None] + rng.uniform(0, 2, size=(g, m))).astype(np.float32)
+    if kind == "wgrad":
+        sb = np.exp2((pr - e)[:, None] + rng.uniform(0, 2, size=(g, n))).astype(np.float32)
+    else:
+        sb = np.exp2((pr - e)[None, :] + rng.uniform(0, 2, size=(n // 128, g))).astype(np.float32)
+    assert np.all(np.isfinite(sa)) and np.all(np.isfinite(sb))
+    assert sa.min() >= 2.0 ** -126 and sb.min() >= 2.0 ** -126
+    return sa, sb
+
+
+@pytest.mark.parametrize("kind", ["fprop", "wgrad"])
+@pytest.mark.parametrize("lo,hi", [(-8, 8), (-125, -100), (90, 100)])
+def test_promoted_scales_across_the_fp32_range(kind, lo, hi):
+    """Max-abs (not power-of-two) scales from about 2^-100 to 2^100 whose
+    per-group products sa*sb stay FP32 normal numbers, including products just
+    above the smallest normal (2^-125..2^-100) and large ones (2^90..2^100):
+    the combined factor of each group is formed in FP32 and must keep the
+    result within the FP32 bound of the oracle, row by row."""
+    fp8q = require_gpu()
+    rng = np.random.default_rng(311 + lo)
+    m, n, k = 256, 256, 1024
+    ops = random_fp8_operands(312, m, n, k, kind=kind)
+    sa, sb = _scale_pairs(rng, kind, m, n, k, lo, hi, spread=100)
+    c = fp8q.fp8_gemm_blockscaled(KINDS[kind], dev(ops["qa"]), dev(sa), dev(ops["qb"]), dev(sb),
+                                  out_dtype=torch.float32)
+    ref = og.gemm_ref(ops["qa"], sa, ops["qb"], sb, kind)
+    got = host(c).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    for r in range(m):
+        assert og.rel_frobenius(got[r], og.round_output(ref[r], "f32")) <= TOL_F32, r
+
+
 def test_wgrad_accumulate_into_fp32():
     fp8q = require_gpu()
     m, n, k = 256, 256, 512
@@ -316,7 +391,7 @@ def test_wgrad_full_size_sampled(layer):
     rr, cc = np.meshgrid(np.arange(ms.size), np.arange(ns.size), indexing="ij")
     ref = og.gemm_ref_entries(qa_r, sa_r, qb_r, sb_r, rr.ravel(), cc.ravel(), "wgrad")
     got = host(dw)[ms][:, ns].ravel().astype(np.float64)
-    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= TOL
+    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= TOL_F32
 
 
 def test_grouped_full_size_sampled():

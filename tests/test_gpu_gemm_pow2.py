@@ -72,7 +72,7 @@ def test_pow2_random_operands(kind, out, mnk):
                                        dev(ops["sb"]), out_dtype=dt)
     ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind)
     err = og.rel_frobenius(_out_host(c), og.round_output(ref, out))
-    assert err <= TOL, err
+    assert err <= (TOL if out == "bf16" else TOL_F32), err
 
 
 def test_pow2_extreme_scale_exponents():
@@ -88,7 +88,7 @@ def test_pow2_extreme_scale_exponents():
     got = _out_host(c)
     # rows are dominated by their largest group scale; compare row by row
     for r in range(0, m, 17):
-        assert og.rel_frobenius(got[r], og.round_output(ref[r], "f32")) <= TOL, r
+        assert og.rel_frobenius(got[r], og.round_output(ref[r], "f32")) <= TOL_F32, r
 
 
 @pytest.mark.parametrize("mask", ["A", "B"])
@@ -141,7 +141,7 @@ def test_one_pow2_operand_accumulate(mask, kind):
     fp8q.fp8_gemm_blockscaled_pow2(KINDS[kind], dev(ops["qa"]), dev(ops["sa"]), dev(ops["qb"]), dev(ops["sb"]), c=c,
                                    accumulate=True, pow2_operands=MASKS[mask])
     ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind) + c0.astype(np.float64)
-    assert og.rel_frobenius(host(c).astype(np.float64), ref) <= TOL
+    assert og.rel_frobenius(host(c).astype(np.float64), ref) <= TOL_F32
 
 
 def test_pow2_wgrad_accumulate_and_k_zero():
@@ -153,7 +153,7 @@ def test_pow2_wgrad_accumulate_and_k_zero():
     fp8q.fp8_gemm_blockscaled_pow2(2, dev(ops["qa"]), dev(ops["sa"]), dev(ops["qb"]), dev(ops["sb"]), c=c,
                                    accumulate=True)
     ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], "wgrad") + c0.astype(np.float64)
-    assert og.rel_frobenius(host(c).astype(np.float64), ref) <= TOL
+    assert og.rel_frobenius(host(c).astype(np.float64), ref) <= TOL_F32
     z = torch.full((256, 256), 7.0, device="cuda")
     e = torch.empty((256, 0), dtype=torch.uint8, device="cuda")
     es = torch.empty((0, 256), dtype=torch.float32, device="cuda")
@@ -216,7 +216,7 @@ def test_wgrad_full_size_pow2_x_operand_only(layer):
     rr, cc = np.meshgrid(np.arange(ms.size), np.arange(ns.size), indexing="ij")
     ref = og.gemm_ref_entries(qa_r, sa_r, qb_r, sb_r, rr.ravel(), cc.ravel(), "wgrad")
     got = host(dw)[ms][:, ns].ravel().astype(np.float64)
-    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= TOL
+    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= TOL_F32
 
 
 def test_pow2_wgrad_full_size_sampled(layer):
@@ -235,7 +235,7 @@ def test_pow2_wgrad_full_size_sampled(layer):
     rr, cc = np.meshgrid(np.arange(ms.size), np.arange(ns.size), indexing="ij")
     ref = og.gemm_ref_entries(qa_r, sa_r, qb_r, sb_r, rr.ravel(), cc.ravel(), "wgrad")
     got = host(dw)[ms][:, ns].ravel().astype(np.float64)
-    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= TOL
+    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= TOL_F32
 
 
 # ----------------------------------------------------------------------------

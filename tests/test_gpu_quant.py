@@ -132,8 +132,10 @@ def test_quant_block(dtype, mode_name, mode, shape):
     assert_bytes_equal(host(s), s_ref, "scales")
     assert_bytes_equal(host(qt), np.ascontiguousarray(q_ref.T), "transposed codes")
     assert_bytes_equal(host(st), np.ascontiguousarray(s_ref.T), "transposed scales")
+    # without the transposed copy (BF16 with cols % 256 == 0 runs the two-block kernel)
     q2, s2 = fp8q.fp8_quant_block(x_dev, mode, transposed=False)
     assert_bytes_equal(host(q2), q_ref, "codes without the transposed copy")
+    assert_bytes_equal(host(s2), s_ref, "scales without the transposed copy")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -161,6 +163,15 @@ def test_degenerate_groups_128x1_and_blocks(dtype, mode_name, mode):
     assert_bytes_equal(host(q), q_ref, "block codes")
     assert_bytes_equal(host(q_t), q_ref.T, "transposed block codes")
     assert_bytes_equal(host(s_t), s_ref.T, "transposed block scales")
+    # the same blocks without the transposed copy: 768 columns, so BF16 input
+    # takes the two-block (128x256 per workgroup) kernel, each degenerate
+    # block in either half of a pair
+    for cols in (slice(0, 768), slice(128, 640)):
+        xs = x_dev[:, cols]
+        q2, s2 = fp8q.fp8_quant_block(xs, mode, transposed=False)
+        q2_ref, s2_ref = oq.quant_128x128(x_ref[:, cols], mode_name)
+        assert_bytes_equal(host(s2), s2_ref, f"block scales, no copy, columns {cols}")
+        assert_bytes_equal(host(q2), q2_ref, f"block codes, no copy, columns {cols}")
 
 
 def test_quant_strided_input_and_outputs():
