@@ -18,12 +18,18 @@ value = useful GEMM FLOP of the step (padding rows excluded) / step time, in
 TFLOP/s; every kernel of the step is inside the timed region.  Per-kernel
 durations come from HIP events recorded on the stream the kernels run on.
 
-After the timed steps, kernels outside the step are timed one by one (their
-entries carry "outside_step"): the single-tiling 1x128 and 128x1 quantizers
-of dY (what the one-pass quantizer replaces), the power-of-two scale mode of
-the activation and weight quantizers, the FP8 -> FP8 1x128 -> 128x1
+After the timed steps, kernels outside the step are timed one by one, each
+after a clean eviction of the memory-side cache (their entries carry
+"outside_step"): the quantizer-only workload as stated (max-abs 1x128 and
+128x1 of the activation, max-abs 128x128 of the weight without the
+transposed copy), the single-tiling 1x128 and 128x1 quantizers of dY (what
+the one-pass quantizer replaces), the power-of-two scale mode of the
+activation and weight quantizers, the FP8 -> FP8 1x128 -> 128x1
 re-quantization of the activation, and the Fprop and Wgrad GEMMs on
 power-of-two operands through the hardware-scaled MFMA path.
+
+cpu_baseline: the CPU oracle timed on this host on a bounded slice of every
+workload (per_config), with the host's core count and CPU model.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--copy-calibration]
@@ -103,6 +109,7 @@ class Step:
                 + pad * N_MOE * 2
             roof_s += max(flop / (PEAK_FP8_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
         self.grouped_roof_us = roof_s * 1e6
+        self.host = host_slices(lin, dy, moe)
         del lin, dy, moe
         dev = self.x.device
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
@@ -157,6 +164,15 @@ class Step:
              gf(self.moe_tokens, N_MOE, D_IN), "flop"),
         ]
         self.extra = [
+            # the activation and weight quantizers of the quantizer-only workload, each on its own
+            ("quant_1x128 X (max-abs)", lambda: q.fp8_quant_tile(self.x, q.TILE_1x128, q.MAXABS, self.qx, self.sx),
+             bf16_quant_bytes(T, D_IN), "bytes"),
+            ("quant_128x1 X (max-abs)", lambda: q.fp8_quant_tile(self.x, q.TILE_128x1, q.MAXABS, self.qxt,
+                                                                 self.sxt),
+             bf16_quant_bytes(T, D_IN), "bytes"),
+            ("quant_128x128 W (max-abs, no transposed copy)", lambda: q.fp8_quant_block(self.wt, q.MAXABS, False,
+                                                                                       self.qw, self.sw),
+             block_bytes(D_OUT, D_IN, False), "bytes"),
             # the two single-tiling calls that the one-pass quantizer of dY replaces (same outputs)
             ("quant_1x128 dY (single tiling)", lambda: q.fp8_quant_tile(self.dy, q.TILE_1x128, q.MAXABS, self.qdy,
                                                                          self.sdy),
@@ -200,26 +216,104 @@ class Step:
                 events[i][1].record()
 
 
-def cpu_baseline():
-    """The oracle, as it stands, on a bounded slice of the Fprop stage."""
+def _host_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_slices(lin, dy, moe):
+    """Host copies of the slices of the same synthetic inputs that cpu_baseline times the oracle on."""
+    starts = np.concatenate([[0], np.cumsum(moe["padded"])])[:4]
+    rows = np.concatenate([np.arange(s0, s0 + 128) for s0 in starts])
+    return {"x": lin["x"][:2048].copy(), "wt": lin["wt"][:4096].copy(),
+            "wt_in": np.ascontiguousarray(lin["wt"][:, :1024]), "dy": dy[:1024].copy(),
+            "dy_t": np.ascontiguousarray(dy[:, :1024]), "x_t": np.ascontiguousarray(lin["x"][:, :1024]),
+            "mx": moe["x"][rows], "mw": np.stack([moe["wt"][e * N_MOE:e * N_MOE + 512] for e in range(4)]),
+            "counts": np.asarray(moe["counts"][:4])}
+
+
+def cpu_baseline(host):
+    """The oracle, as it stands, timed on this host's cores on a bounded slice of every workload.
+
+    Operand preparation (widening, and the oracle's own quantization of the GEMM operand slices) is outside
+    the timed parts; each GEMM line times the exact per-K-group product of its slice.  The headline value is the
+    Fprop slice's rate; every line is in per_config."""
     from threadpoolctl import threadpool_info
     from oracle import gemm as og, quant as oq
-    from workloads import bf16_bits_as_f32, linear_layer
-    m, n = 3072, 12288
-    d = linear_layer()
-    x = bf16_bits_as_f32(d["x"][:m])
-    wt = bf16_bits_as_f32(d["wt"][:n])
-    del d
-    t0 = time.perf_counter()
-    qa, sa = oq.quant_1x128(x)
-    qb, sb = oq.quant_128x128(wt)
-    og.gemm_ref(qa, sa, qb, sb, og.FPROP)
-    dt = time.perf_counter() - t0
-    flop = 2.0 * m * n * D_IN
+    from workloads import bf16_bits_as_f32, tiny_fprop
+    lines = []
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def add(config, kernel, secs, work, kind, sample):
+        rate = work / secs / (1e12 if kind == "flop" else 1e9)
+        lines.append({"config": config, "kernel": kernel, "oracle_s": round(secs, 3),
+                      "rate": round(rate, 5), "unit": "TFLOP/s" if kind == "flop" else "GB/s", "sample": sample})
+
+    # tiny Fprop: quantize both operands and multiply, whole problem
+    d = tiny_fprop()
+    def tiny():
+        qa, sa = oq.quant_1x128(d["a"])
+        qb, sb = oq.quant_128x128(d["bt"])
+        og.gemm_ref(qa, sa, qb, sb, og.FPROP, exact_int=True)
+    add("tiny Fprop 128x256x128", "quant 1x128 + 128x128 + Fprop (int64)", timed(tiny), 2.0 * 128 * 128 * 256, "flop",
+        "whole problem")
+    # quantizer-only workload: 2048 of the 8192 activation rows, 2048 of the 18432 weight rows
+    x = bf16_bits_as_f32(host["x"][:2048])
+    qbytes = x.size * 2 + x.size + x.size // 128 * 4
+    add("quantizer-only", "quant_1x128 X (max-abs)", timed(lambda: oq.quant_1x128(x)), qbytes, "bytes",
+        "X rows 0..2047 of 8192")
+    add("quantizer-only", "quant_1x128 X (pow2)", timed(lambda: oq.quant_1x128(x, oq.MODE_POW2)), qbytes, "bytes",
+        "X rows 0..2047 of 8192")
+    add("quantizer-only", "quant_128x1 X (max-abs)", timed(lambda: oq.quant_128x1(x)), qbytes, "bytes",
+        "X rows 0..2047 of 8192")
+    w = bf16_bits_as_f32(host["wt"][:2048])
+    add("quantizer-only", "quant_128x128 W (max-abs)", timed(lambda: oq.quant_128x128(w)),
+        w.size * 3 + (w.size // 16384) * 4, "bytes", "W rows 0..2047 of 18432")
+    # Fprop: 2048 tokens x 4096 output channels, full K = 7168
+    qa, sa = oq.quant_1x128(bf16_bits_as_f32(host["x"]))
+    qb, sb = oq.quant_128x128(bf16_bits_as_f32(host["wt"]))
+    f_s = timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.FPROP))
+    f_flop = 2.0 * qa.shape[0] * qb.shape[0] * D_IN
+    add("Fprop", "gemm Fprop", f_s, f_flop, "flop", f"M={qa.shape[0]} of 8192, N={qb.shape[0]} of 18432, K={D_IN}")
+    # Dgrad: 1024 tokens x 1024 input channels, full K = 18432
+    qa, sa = oq.quant_1x128(bf16_bits_as_f32(host["dy"]))
+    qb, sb = oq.quant_128x128(np.ascontiguousarray(bf16_bits_as_f32(host["wt_in"]).T))
+    add("Dgrad + Wgrad", "gemm Dgrad", timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.DGRAD)),
+        2.0 * qa.shape[0] * qb.shape[0] * D_OUT, "flop", f"M=1024 of 8192, N=1024 of 7168, K={D_OUT}")
+    # Wgrad: 1024 output x 1024 input channels, full K = 8192 tokens
+    qa, sa = oq.quant_128x1(bf16_bits_as_f32(host["dy_t"]))
+    qb, sb = oq.quant_128x1(bf16_bits_as_f32(host["x_t"]))
+    add("Dgrad + Wgrad", "gemm Wgrad", timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.WGRAD)),
+        2.0 * qa.shape[0] * qb.shape[0] * T, "flop", f"M=1024 of 18432, N=1024 of 7168, K={T}")
+    # grouped: the first 128-row tile of experts 0..3, N = 512 of 2048 (real rows only in the FLOP count)
+    qa, sa = oq.quant_1x128(bf16_bits_as_f32(host["mx"]))
+    qbs = [oq.quant_128x128(bf16_bits_as_f32(wv)) for wv in host["mw"]]
+    qb = np.stack([q_ for q_, _ in qbs])
+    sb = np.stack([s_ for _, s_ in qbs])
+    gmap = np.arange(4, dtype=np.int32)
+    real = sum(min(128, int(c)) for c in host["counts"])
+    add("grouped MoE", "gemm grouped MoE", timed(lambda: og.grouped_ref(qa, sa, qb, sb, gmap)),
+        2.0 * real * 512 * D_IN, "flop", "first 128-row tile of experts 0..3, N=512 of 2048, K=7168")
+
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": max(blas + [1]), "kind": "oracle",
-            "sample": f"Fprop slice M={m} tokens, N={n}, K={D_IN}: oracle 1x128 + 128x128 quantization of "
-                      f"the slices and the exact per-K-group GEMM, {dt:.2f} s"}
+    head = next(l for l in lines if l["kernel"] == "gemm Fprop")
+    return {"value": head["rate"], "unit": "TFLOP/s", "cores": max(blas + [1]), "kind": "oracle",
+            "sample": f"Fprop slice {head['sample']}: the oracle's exact per-K-group GEMM, {head['oracle_s']} s "
+                      f"(every workload's slice in per_config)",
+            "nproc": os.cpu_count(), "host_cpu": _host_model(),
+            "threads_note": "numpy elementwise work (the quantizers) runs on one thread; the per-group FP64 "
+                            "matmuls use the BLAS threads given in cores",
+            "oracle_s_total": round(sum(l["oracle_s"] for l in lines), 2), "per_config": lines}
 
 
 def main():
@@ -322,7 +416,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"] = cpu_baseline(step.host)
     print(json.dumps(result), flush=True)
 
 
@@ -337,10 +431,10 @@ def _kernel_entry(us, work, kind):
 
 def _roofline(name, k):
     """Roofline entry of the dominant kernel.  traffic (calibrated HBM bytes per launch) and, for an MFMA-bound
-    kernel, its average shader clock come from profiles/hbm_traffic.json, and only while that file's kernel
-    source hash matches; frac_at_clock sets the achieved rate against the published peak scaled from its
-    2.4 GHz to that clock."""
-    traffic, clock = None, None
+    kernel, its average shader clock come from profiles/hbm_traffic.json, and its matrix-core busy fraction from
+    profiles/gemm_counters.json, each only while that file's kernel source hash matches; frac_at_clock sets the
+    achieved rate against the published peak scaled from its 2.4 GHz to that clock."""
+    traffic, clock, util = None, None, None
     tpath = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if os.path.exists(tpath):
         with open(tpath) as fh:
@@ -348,6 +442,12 @@ def _roofline(name, k):
         if t.get("source_hash") == source_hash():
             traffic = t.get("kernels", {}).get(name)
             clock = t.get("clock_ghz", {}).get(name)
+    cpath = os.path.join(ROOT, "profiles", "gemm_counters.json")
+    if os.path.exists(cpath):
+        with open(cpath) as fh:
+            c = json.load(fh)
+        if c.get("source_hash") == source_hash():
+            util = c.get("gemms", {}).get(name)
     if "tflops" in k:
         r = {"kernel": name, "bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
              "unit": "TFLOP/s", "frac": round(k["tflops"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
@@ -355,6 +455,11 @@ def _roofline(name, k):
         if clock:
             r["clock_ghz"] = clock
             r["frac_at_clock"] = round(k["tflops"] / (PEAK_FP8_TFLOPS * clock / PEAK_CLOCK_GHZ), 4)
+        if util:
+            # matrix-core busy fraction of all SIMD cycles, and the VALU work beside it (rocprofv3 counters)
+            r["mfma_busy"] = util["mfma_busy"]
+            r["valu_insts_per_mfma"] = util["valu_insts_per_mfma"]
+            r["valu_busy_est"] = util["valu_busy_est"]
         return r
     return {"kernel": name, "bound": "hbm", "achieved": k["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(k["gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic, "avg_us": k["us"]}

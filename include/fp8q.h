@@ -25,6 +25,11 @@
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the
  *     library allocates nothing and keeps no state between calls, so calls
  *     are thread-safe.
+ *   - Status codes and enum-valued arguments (dtype, tile, scale mode, GEMM
+ *     kind, power-of-two operand mask) are passed as plain int, so that the
+ *     ABI does not depend on the size a C compiler picks for an enum; the
+ *     FP8Q_* constants below are the valid values, anything else returns
+ *     FP8Q_ERR_ARG.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All work
  *     is enqueued on it; the library never synchronises.
  *   - Return value: an fp8q_status.  Arguments are validated before anything
@@ -76,6 +81,12 @@ typedef enum { FP8Q_POW2_A = 1, FP8Q_POW2_B = 2, FP8Q_POW2_AB = 3 } fp8q_pow2_op
 
 /*
  * fp8_quant_tile -- online 1x128 or 128x1 tile quantization.
+ * [dssusan.co.kr FP8 excerpt, paragraph 4: activations grouped per token per
+ *  128 channels (1x128), re-tiled 1x128 -> 128x1 for the backward pass;
+ *  paragraph 2: each tile's max-abs computed online and the scale derived
+ *  from it; "Deepseek - Not For everyone", paragraph 3: the max-abs is mapped
+ *  onto the largest FP8 value; dssusan.co.kr, paragraph 1: optional integral
+ *  power-of-2 scales]
  *
  * x        : input X[rows][cols], leading dimension ld_x (elements), dtype x_dtype.
  * tile     : FP8Q_TILE_1x128 -- groups of 128 consecutive columns in one row
@@ -169,8 +180,17 @@ int fp8_quant_tile_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, 
  * c        : C[M][N], leading dimension ldc (elements), dtype c_dtype
  *            (FP8Q_BF16, rounded to nearest-even, or FP8Q_F32).
  * accumulate : 0 -> C = result; 1 -> C += result (FP8Q_F32 output only).
- * Requires M, N, K multiples of 128.  M == 0 or N == 0 is a no-op;
- * K == 0 with M, N > 0 writes zeros (or leaves C unchanged with accumulate).
+ * Requires M, N, K multiples of 128, and lda, ldb of at most 4,194,176 bytes
+ * (the kernels address a tile's rows with 32-bit offsets); otherwise
+ * FP8Q_ERR_UNSUPPORTED.  M == 0 or N == 0 is a no-op; K == 0 with M, N > 0
+ * writes zeros (or leaves C unchanged with accumulate).
+ * Scale domain: each group's combined factor sa*sb is formed in FP32 (for
+ * WGRAD per element, for FPROP / DGRAD per row and block) and multiplied into
+ * the FP32 accumulation with one FMA; results follow the definition above to
+ * FP32 rounding as long as every such product is an FP32 normal number
+ * (2^-126 <= sa*sb < 2^128) and the output is finite.  Scales from
+ * fp8_quant_tile / fp8_quant_block of data whose max-abs values lie between
+ * about 2^-55 and 2^55 always satisfy this.
  */
 int fp8_gemm_blockscaled(int kind, int64_t M, int64_t N, int64_t K,
                          const uint8_t* a, int64_t lda, const float* a_scales,

@@ -10,6 +10,10 @@
 namespace {
 
 constexpr int64_t kMaxGridX = 0x7FFFFFFF;
+// GEMM operands are read through buffer resources with 32-bit offsets within
+// a tile of up to 512 rows: leading dimensions of A and B must stay below
+// 2^31 / 512 bytes (4 MiB), with K <= ld.
+constexpr int64_t kMaxGemmLd = (int64_t(1) << 31) / 512 - 128;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -69,6 +73,7 @@ int check_gemm(int kind, int64_t M, int64_t N, int64_t K, const uint8_t* a, int6
     return FP8Q_ERR_ALIGN;
   if (M % 128 || N % 128 || K % 128) return FP8Q_ERR_UNSUPPORTED;
   if (accumulate && c_dtype != FP8Q_F32) return FP8Q_ERR_UNSUPPORTED;
+  if (K > 0 && (lda > kMaxGemmLd || ldb > kMaxGemmLd)) return FP8Q_ERR_UNSUPPORTED;
   if (N / 128 > kMaxGridX / (M / 128)) return FP8Q_ERR_UNSUPPORTED;   // tiles beyond one grid
   int64_t nsa = 0, nsb = 0;
   if (!mul_ok(K / 128, M, &nsa) || !mul_ok(K / 128, N, &nsb)) return FP8Q_ERR_SHAPE;
@@ -279,6 +284,7 @@ int fp8_gemm_blockscaled_grouped(int32_t num_groups, int64_t M_total, int64_t N,
   if (K > 0 && (!aligned16(a) || !aligned16(b) || !aligned16(a_scales) || !aligned16(b_scales) || lda % 16))
     return FP8Q_ERR_ALIGN;
   if (M_total % 128 || N % 128 || K % 128) return FP8Q_ERR_UNSUPPORTED;
+  if (K > 0 && (lda > kMaxGemmLd || K > kMaxGemmLd)) return FP8Q_ERR_UNSUPPORTED;
   if (N / 128 > kMaxGridX / (M_total / 128)) return FP8Q_ERR_UNSUPPORTED;   // tiles beyond one grid
   int64_t nsa = 0, nsb = 0, brows = 0;
   if (!mul_ok(K / 128, M_total, &nsa) || !mul_ok(N / 128, K / 128, &nsb) ||

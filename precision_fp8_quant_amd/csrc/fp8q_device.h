@@ -27,9 +27,13 @@ struct ScalePair {
 };
 
 // fl32(a / 448) for a >= 448 * 2^-126.  448 = 7 * 2^6, so a/448 is fl32(a/7)
-// scaled exactly by 2^-6; fl32(a/7) is the product with fl32(1/7) plus one
-// FMA residual correction.  Checked bit-exact against IEEE division for every
-// float32 in [448 * 2^-126, FLT_MAX] on gfx950.
+// scaled exactly by 2^-6.  fl32(a/7) comes from the quotient estimate
+// q0 = a * fl32(1/7), its exact residual r = a - 7*q0 (one FMA) and the
+// corrected quotient q0 + r * fl32(1/7) (one more FMA): Markstein's
+// FMA-based final correction for IEEE division (P. W. Markstein,
+// "Computation of elementary functions on the IBM RISC System/6000
+// processor", IBM J. Res. Develop. 34(1), 1990).  Checked bit-exact against
+// IEEE division for every float32 in [448 * 2^-126, FLT_MAX] on gfx950.
 __device__ __forceinline__ float div_by_448(float a) {
   const float c = __uint_as_float(0x3E124925u);          // fl32(1/7)
   const float q0 = a * c;
@@ -37,10 +41,12 @@ __device__ __forceinline__ float div_by_448(float a) {
   return __builtin_fmaf(r, c, q0) * 0.015625f;
 }
 
-// fl32(448 / a) for a >= 448 * 2^-126: hardware reciprocal, one FMA residual
-// correction.  For a > 2^100 the computation runs on a * 2^-64 (so 1/a stays
-// a normal number) and the result is scaled back exactly.  Checked bit-exact
-// against IEEE division for every float32 in [448 * 2^-126, FLT_MAX] on gfx950.
+// fl32(448 / a) for a >= 448 * 2^-126: the hardware reciprocal estimate
+// y ~ 1/a, q0 = 448 * y, then the same Markstein correction q0 + r * y with
+// the residual r = 448 - a*q0 formed exactly by an FMA.  For a > 2^100 the
+// computation runs on a * 2^-64 (so 1/a stays a normal number) and the
+// result is scaled back exactly.  Checked bit-exact against IEEE division for
+// every float32 in [448 * 2^-126, FLT_MAX] on gfx950.
 __device__ __forceinline__ float div_448_by(float a0) {
   const bool big = a0 > 0x1p+100f;
   const float a = big ? a0 * 0x1p-64f : a0;

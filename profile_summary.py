@@ -15,7 +15,19 @@ figure is the mean over the timed calls.
       counters read for the plain 1 GiB copy) and the GEMMs' average shader clock
       (GRBM_GUI_ACTIVE / (8 XCDs x duration)) -> profiles/hbm_traffic.json + markdown on stdout
 
+  python profile_summary.py counters BENCH_JSON MFMA_DIR WAIT_DIR --steps K
+      per-GEMM matrix-core utilisation from two SQ counter runs (MFMA_PASS, WAIT_PASS
+      below) -> profiles/gemm_counters.json + markdown on stdout
+
 BENCH_JSON is a file holding the bench's JSON line (any run of the same tree).
+
+Counter units on gfx950, as read here: GRBM_GUI_ACTIVE adds the busy cycles of
+the 8 XCDs; SQ_VALU_MFMA_BUSY_CYCLES adds, over every SIMD, the cycles its
+matrix core is busy (32 per v_mfma_*_16x16x128_f8f6f4); SQ_INSTS_* count
+instructions over all waves; SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_ANY
+count wave cycles in units of 4.  MFMA busy = MFMA busy cycles / (SIMDs x
+GRBM_GUI_ACTIVE / 8); the VALU estimate charges each non-MFMA VALU
+instruction 4 cycles (a wave64 FP32 operation on a 16-lane SIMD).
 """
 
 import argparse
@@ -39,6 +51,13 @@ FAMILIES = [
 ]
 COPY = "calibration copy 1 GiB"
 XCDS = 8
+SIMDS = 256 * 4        # MI355X: 256 compute units of 4 SIMDs
+# the two counter passes of the `counters` command (each within the per-pass
+# limits: at most 8 SQ and 2 GRBM counters)
+MFMA_PASS = ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU",
+             "SQ_INSTS_MFMA", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES"]
+WAIT_PASS = ["GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+             "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_SALU", "SQ_BUSY_CYCLES", "SQ_INSTS_SMEM"]
 
 
 def family(bench_name):
@@ -226,6 +245,73 @@ def cmd_traffic(a):
     print(f"Kernel sources hash: `{out['source_hash']}`")
 
 
+def compute_counters(bench, mfma_rows, wait_rows, steps, source_hash):
+    """gemm_counters.json content: per GEMM bench call, the counters summed over its grids and averaged over
+    the timed calls, and the derived utilisation figures."""
+    runs = {"mfma": match(bench, dispatches(mfma_rows), steps)[0],
+            "wait": match(bench, dispatches(wait_rows), steps)[0]}
+    out = {}
+    for n, calls in runs["mfma"].items():
+        if not n.startswith("gemm"):
+            continue
+        c = {}
+        for key, passes in (("mfma", MFMA_PASS), ("wait", WAIT_PASS)):
+            for name in passes:
+                vals = [sum(d["counters"].get(name, 0.0) for d in call) for call in runs[key][n]]
+                c[f"{name}@{key}"] = statistics.mean(vals)
+        gui_m, gui_w = c["GRBM_GUI_ACTIVE@mfma"], c["GRBM_GUI_ACTIVE@wait"]
+        simd_cycles = SIMDS * gui_m / XCDS
+        mfma = c["SQ_INSTS_MFMA@mfma"]
+        valu_other = c["SQ_INSTS_VALU@mfma"] - mfma
+        wave = c["SQ_WAVE_CYCLES@wait"]
+        us = statistics.mean(dur_us(call) for call in runs["mfma"][n])
+        flop = bench["kernels"][n].get("flop")
+        out[n] = {
+            "counters": {k: round(v, 1) for k, v in c.items()},
+            "dispatch_us_under_counters": round(us, 1),
+            "clock_ghz": round(gui_m / (XCDS * us * 1e3), 3),
+            "mfma_busy": round(c["SQ_VALU_MFMA_BUSY_CYCLES@mfma"] / simd_cycles, 4),
+            "mfma_f8_flop": c["SQ_INSTS_VALU_MFMA_MOPS_F8@mfma"] * 512,
+            "algorithmic_flop": flop,
+            "valu_insts_per_mfma": round(valu_other / mfma, 3) if mfma else None,
+            "valu_busy_est": round(4 * valu_other / simd_cycles, 4),
+            "coexec_of_mfma_busy": round(c["SQ_VALU_MFMA_COEXEC_CYCLES@mfma"] / c["SQ_VALU_MFMA_BUSY_CYCLES@mfma"], 4)
+            if c["SQ_VALU_MFMA_BUSY_CYCLES@mfma"] else None,
+            "lds_bank_conflict_cycles": c["SQ_LDS_BANK_CONFLICT@mfma"],
+            "lds_insts_per_mfma": round(c["SQ_INSTS_LDS@mfma"] / mfma, 3) if mfma else None,
+            "wave_issuing": round(c["SQ_ACTIVE_INST_ANY@wait"] / wave, 4) if wave else None,
+            "wave_waiting_on_counters": round(c["SQ_WAIT_ANY@wait"] / wave, 4) if wave else None,
+            "wave_waiting_to_issue": round(c["SQ_WAIT_INST_ANY@wait"] / wave, 4) if wave else None,
+            "clock_ghz_wait_pass": round(gui_w / (XCDS * statistics.mean(dur_us(call) for call in runs["wait"][n])
+                                                  * 1e3), 3),
+        }
+    cmd = "rocprofv3 --pmc {} -d <dir> --output-format csv -- python3 -u bench.py --steps %d --warmup 1 " \
+          "--no-cpu-baseline" % steps
+    return {"source_hash": source_hash, "mfma_command": cmd.format(" ".join(MFMA_PASS)),
+            "wait_command": cmd.format(" ".join(WAIT_PASS)), "gemms": out}
+
+
+def cmd_counters(a):
+    sys.path.insert(0, ROOT)
+    from bench import source_hash
+    bench = read_bench(a.bench)
+    out = compute_counters(bench, read_csv(a.mfma_dir, "counter_collection"),
+                           read_csv(a.wait_dir, "counter_collection"), a.steps, source_hash())
+    with open(os.path.join(ROOT, "profiles", "gemm_counters.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print("| GEMM | us (under counters) | clock GHz | MFMA busy | VALU instr. / MFMA | VALU busy (est.) | "
+          "co-issued with MFMA | LDS bank-conflict cycles | LDS instr. / MFMA | wave issuing / waiting on "
+          "counters / waiting to issue |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for n, g in out["gemms"].items():
+        print(f"| {n} | {g['dispatch_us_under_counters']:.1f} | {g['clock_ghz']:.2f} | {g['mfma_busy']:.3f} | "
+              f"{g['valu_insts_per_mfma']:.2f} | {g['valu_busy_est']:.3f} | {g['coexec_of_mfma_busy']:.3f} | "
+              f"{g['lds_bank_conflict_cycles']:.0f} | {g['lds_insts_per_mfma']:.2f} | "
+              f"{g['wave_issuing']:.2f} / {g['wave_waiting_on_counters']:.2f} / {g['wave_waiting_to_issue']:.2f} |")
+    print()
+    print(f"Kernel sources hash: `{out['source_hash']}`")
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -239,8 +325,13 @@ def main():
     f.add_argument("write_dir")
     f.add_argument("clock_dir")
     f.add_argument("--steps", type=int, required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("bench")
+    c.add_argument("mfma_dir")
+    c.add_argument("wait_dir")
+    c.add_argument("--steps", type=int, required=True)
     a = p.parse_args()
-    cmd_trace(a) if a.cmd == "trace" else cmd_traffic(a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

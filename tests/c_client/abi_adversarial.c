@@ -89,9 +89,12 @@ int main(void) {
   EXPECT(fp8_gemm_blockscaled(FP8Q_FPROP, BIG, 128, 128, B, 128, C, E, 128, D, F, FP8Q_BF16, 128, 0, NULL),
          FP8Q_ERR_UNSUPPORTED);                               /* more tiles than one grid */
   EXPECT(fp8_gemm_blockscaled(FP8Q_FPROP, 128 * 128, 128, BIG, B, BIG, C, E, BIG, D, F, FP8Q_BF16, 128, 0, NULL),
-         FP8Q_ERR_SHAPE);                                     /* scale counts overflow */
+         FP8Q_ERR_UNSUPPORTED);                               /* rows of A and B beyond 32-bit tile offsets */
   EXPECT(fp8_gemm_blockscaled(FP8Q_FPROP, 256, 256, 256, B, HUGE_LD, C, E, 256, D, F, FP8Q_BF16, 256, 0, NULL),
-         FP8Q_ERR_SHAPE);                                     /* A extent overflows */
+         FP8Q_ERR_UNSUPPORTED);
+  EXPECT(fp8_gemm_blockscaled(FP8Q_DGRAD, 256, 256, 256, B, 256, C, E, (int64_t)1 << 22, D, F, FP8Q_BF16, 256, 0,
+                              NULL),
+         FP8Q_ERR_UNSUPPORTED);                               /* ldb of 4 MiB */
   EXPECT(fp8_gemm_blockscaled(FP8Q_WGRAD, 256, 256, 256, B, 256, C, E, 256, D, F, FP8Q_F32, HUGE_LD, 0, NULL),
          FP8Q_ERR_SHAPE);                                     /* C extent overflows */
   EXPECT(fp8_gemm_blockscaled(FP8Q_WGRAD, 256, 256, 256, B, 256, C, E, 256, D, F, FP8Q_F32, INT64_MAX - 1, 0, NULL),

@@ -143,6 +143,8 @@ def test_gemm_validation(fn):
     assert _gemm(fn, b=C + 8) == fp8q.ERR_ALIGN
     assert _gemm(fn, M=200) == fp8q.ERR_UNSUPPORTED
     assert _gemm(fn, acc=1) == fp8q.ERR_UNSUPPORTED              # accumulate needs FP32 output
+    assert _gemm(fn, lda=1 << 22) == fp8q.ERR_UNSUPPORTED         # rows of 4 MiB: beyond 32-bit tile offsets
+    assert _gemm(fn, ldb=(1 << 22) - 112) == fp8q.ERR_UNSUPPORTED      # just above 4,194,176
     assert _gemm(fn, c=A + 4096) == fp8q.ERR_ALIAS
 
 

@@ -88,3 +88,46 @@ def test_traffic_is_calibrated_on_the_copy_and_sums_the_grids():
     assert out["clock_ghz"]["gemm Dgrad"] == pytest.approx(round((1001 + 10 + 1002 + 10) / (8 * 20000), 3))
     assert set(out["clock_ghz"]) == {"gemm Dgrad"}
     assert out["source_hash"] == "hash"
+
+
+def _multi_rows(steps, warmup, values):
+    """Dispatch rows carrying several counters per dispatch: values[name] for the GEMM's first grid (its second
+    grid carries a tenth of each)."""
+    rows = []
+    for r in _rows(steps, warmup, "GRBM_GUI_ACTIVE"):
+        for name, v in values.items():
+            rr = dict(r, Counter_Name=name)
+            if r["Kernel_Name"] == GEMM_A:
+                rr["Counter_Value"] = str(v)
+            elif r["Kernel_Name"] == GEMM_B:
+                rr["Counter_Value"] = str(v / 10)
+            else:
+                rr["Counter_Value"] = "1.0"
+            rows.append(rr)
+    return rows
+
+
+def test_counters_derive_mfma_busy_and_wait_split():
+    steps, warmup = 2, 1
+    # per dispatch of the first grid: 8000 ns at GUI 8*16000 cycles = 2 GHz; 1000 MFMAs busy 32 cycles each
+    mfma = {"GRBM_GUI_ACTIVE": 128000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 32000.0, "SQ_INSTS_VALU_MFMA_MOPS_F8": 128000.0,
+            "SQ_INSTS_VALU": 6000.0, "SQ_INSTS_MFMA": 1000.0, "SQ_VALU_MFMA_COEXEC_CYCLES": 16000.0,
+            "SQ_LDS_BANK_CONFLICT": 0.0, "SQ_INSTS_LDS": 750.0, "SQ_WAVE_CYCLES": 100.0}
+    wait = {"GRBM_GUI_ACTIVE": 128000.0, "SQ_WAVE_CYCLES": 100.0, "SQ_WAIT_ANY": 30.0, "SQ_WAIT_INST_ANY": 40.0,
+            "SQ_ACTIVE_INST_ANY": 30.0, "SQ_LDS_IDX_ACTIVE": 1.0, "SQ_INSTS_SALU": 1.0, "SQ_BUSY_CYCLES": 1.0,
+            "SQ_INSTS_SMEM": 1.0}
+    bench = {"kernels": dict(BENCH["kernels"])}
+    bench["kernels"]["gemm Dgrad"] = {"us": 900.0, "flop": 1.0}
+    out = ps.compute_counters(bench, _multi_rows(steps, warmup, mfma), _multi_rows(steps, warmup, wait), steps, "h")
+    g = out["gemms"]["gemm Dgrad"]
+    # the two grids of a call are summed: counters x 1.1, duration 8000 + 2000 ns
+    assert g["counters"]["SQ_VALU_MFMA_BUSY_CYCLES@mfma"] == pytest.approx(35200.0)
+    assert g["mfma_busy"] == pytest.approx(35200.0 / (ps.SIMDS * 140800.0 / 8), abs=1e-4)
+    assert g["clock_ghz"] == pytest.approx(140800.0 / (8 * 10000.0), abs=1e-3)
+    assert g["mfma_f8_flop"] == pytest.approx(140800.0 * 512)
+    assert g["valu_insts_per_mfma"] == pytest.approx(5.0)
+    assert g["coexec_of_mfma_busy"] == pytest.approx(0.5)
+    assert g["lds_insts_per_mfma"] == pytest.approx(0.75)
+    assert (g["wave_issuing"], g["wave_waiting_on_counters"], g["wave_waiting_to_issue"]) == \
+        pytest.approx((0.3, 0.3, 0.4))
+    assert set(out["gemms"]) == {"gemm Dgrad"}
