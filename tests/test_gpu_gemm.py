@@ -247,18 +247,28 @@ def test_grouped_small(n):
     assert np.all(h[128:256] == 3.0)
     keep = np.r_[0:128, 256:640]
     assert og.rel_frobenius(h[keep], ref[keep]) <= TOL_F32
+    # two neighbouring tiles with an out-of-range id: both skipped
+    gmap3 = gmap.copy()
+    gmap3[0:2] = 9
+    c3 = torch.full((128 * gmap.size, n), 3.0, dtype=torch.float32, device="cuda")
+    fp8q.fp8_gemm_blockscaled_grouped(dev(gmap3), dev(qa), dev(sa), dev(qb), dev(sb), c=c3)
+    h3 = host(c3)
+    assert np.all(h3[0:256] == 3.0)
+    assert og.rel_frobenius(h3[256:], ref[256:]) <= TOL_F32
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-def test_grouped_tail_balanced_two_grid_launch(out):
-    """65 M-tiles x N=2048: 260 tiles of 128x512 on 256 CUs, so the last M-tile
-    runs as a second grid of 128x256 tiles (its A rows, A scales, group ids and
-    C rows offset); every output is checked, both grids separately."""
+@pytest.mark.parametrize("n", [2048, 768])
+def test_grouped_tail_balanced_two_grid_launch(out, n):
+    """65 M-tiles in runs of one group: with N=2048, 260 tiles of 128x512 on 256
+    CUs, so the last M-tile runs as a second grid of 128x256 tiles (its A rows,
+    A scales, group ids and C rows offset); with N=768, one grid of 128x256
+    tiles.  Every 128-row tile is checked on its own."""
     fp8q = require_gpu()
     rng = np.random.default_rng(91)
-    g, n, k, tiles_m = 4, 2048, 256, 65
-    gmap = rng.integers(0, g, size=tiles_m).astype(np.int32)
-    gmap[-1] = 3                                   # the split-off tile uses a group of its own choosing
+    g, k, tiles_m = 4, 256, 65
+    gmap = np.repeat(rng.integers(0, g, size=(tiles_m + 2) // 3), 3)[:tiles_m].astype(np.int32)  # runs of 3
+    gmap[10] = (gmap[10] + 1) % g                  # a lone tile inside a run
     ops = random_fp8_operands(92, 128 * tiles_m, n * g, k)
     qa, sa = ops["qa"], ops["sa"]
     qb = ops["qb"].reshape(g, n, k)
@@ -271,8 +281,9 @@ def test_grouped_tail_balanced_two_grid_launch(out):
         c = torch.empty((128 * tiles_m, n), dtype=torch.float32, device="cuda")
         fp8q.fp8_gemm_blockscaled_grouped(dev(gmap), dev(qa), dev(sa), dev(qb), dev(sb), c=c)
         got, want, tol = host(c).astype(np.float64), ref, TOL_F32
-    for rows in (slice(0, 128 * 64), slice(128 * 64, 128 * tiles_m)):   # first grid, second grid
-        assert og.rel_frobenius(got[rows], want[rows]) <= tol, rows
+    for t in range(tiles_m):
+        rows = slice(128 * t, 128 * (t + 1))
+        assert og.rel_frobenius(got[rows], want[rows]) <= tol, t
 
 
 def test_grouped_runs_dealt_to_xcds_over_several_rounds():
