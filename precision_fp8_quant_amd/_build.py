@@ -62,5 +62,18 @@ def build(verbose=False, extra_flags=()):
     return LIB_PATH
 
 
+TEST_PROBE_SRC = os.path.join(os.path.dirname(PKG_DIR), "tests", "hip", "scale_div_probe.hip")
+TEST_PROBE_LIB = os.path.join(os.path.dirname(PKG_DIR), "tests", "hip", "libfp8q_divprobe.so")
+
+
+def build_test_probe(verbose=False):
+    """Compile the GPU test helper tests/hip/scale_div_probe.hip (not part of libfp8q.so) with the library's
+    device flags, so that it exercises the same code as the quantizers."""
+    tmp = TEST_PROBE_LIB + ".tmp"
+    _run([HIPCC, *COMMON_FLAGS, *DEVICE_FLAGS, "-shared", TEST_PROBE_SRC, "-o", tmp], verbose)
+    os.replace(tmp, TEST_PROBE_LIB)
+    return TEST_PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
