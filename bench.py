@@ -28,6 +28,10 @@ activation and weight quantizers, the FP8 -> FP8 1x128 -> 128x1
 re-quantization of the activation, and the Fprop and Wgrad GEMMs on
 power-of-two operands through the hardware-scaled MFMA path.
 
+vendor_gemm_context: the ROCm library's FP8 GEMM (hipBLASLt) on the Fprop
+shape and codes, with per-tensor and with MX scales (it offers no 1x128 /
+128x128 block scaling on ROCm), for context; not part of the step.
+
 cpu_baseline: the CPU oracle timed on this host on a bounded slice of every
 workload (per_config), with the host's core count and CPU model.
 
@@ -388,6 +392,8 @@ def main():
                                                 outside_step=True)
     del src, dst
 
+    vendor = vendor_gemm_context(step, args.steps, per_kernel)
+
     g = per_kernel["gemm grouped MoE"]
     g["per_expert_roof_us"] = round(step.grouped_roof_us, 1)
     g["per_expert_roof_frac"] = round(step.grouped_roof_us / g["us"], 4)
@@ -413,11 +419,53 @@ def main():
         "kernels": per_kernel,
         "roofline": roof,
         "cpu_baseline": None,
+        "vendor_gemm_context": vendor,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(step.host)
     print(json.dumps(result), flush=True)
+
+
+def vendor_gemm_context(step, steps, per_kernel):
+    """The ROCm library's own FP8 GEMM (hipBLASLt, through torch's scaled matrix multiply) on the Fprop shape and
+    the same E4M3 codes, for context: it has no 1x128 / 128x128 block scaling on ROCm, so it runs with one scale
+    per tensor (no per-group work at all) and with MX scales (one E8M0 exponent per 32 K values in the matrix core,
+    the library's counterpart of the hardware-scaled path).  Not part of the step or of the path."""
+    import torch.nn.functional as F
+    qa = step.qx.view(torch.float8_e4m3fn)
+    qb = step.qw.view(torch.float8_e4m3fn).t()
+    one = torch.ones((), dtype=torch.float32, device="cuda")
+    e8 = lambda rows: torch.full((rows, D_IN // 32), 1.0, device="cuda").to(torch.float8_e8m0fnu)
+    ea, eb = e8(T), e8(D_OUT)
+    cases = {
+        "per-tensor scales": (lambda: torch._scaled_mm(qa, qb, scale_a=one, scale_b=one, out_dtype=torch.bfloat16),
+                              "gemm Fprop"),
+        "MX scales (E8M0 per 32 K, in the matrix core)": (
+            lambda: F.scaled_mm(qa, qb, ea, F.ScalingType.BlockWise1x32, eb, F.ScalingType.BlockWise1x32,
+                                F.SwizzleType.NO_SWIZZLE, F.SwizzleType.NO_SWIZZLE),
+            "gemm Fprop pow2 (hardware-scaled MFMA)"),
+    }
+    out = {"library": "hipBLASLt (torch scaled_mm)", "shape": f"M={T} N={D_OUT} K={D_IN}, BF16 out",
+           "operands": "the step's Fprop E4M3 codes", "cases": {}}
+    for name, (fn, ours) in cases.items():
+        try:
+            for _ in range(2):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+            e = _kernel_entry(us, 2.0 * T * D_OUT * D_IN, "flop")
+            e["ours"] = ours
+            e["library_us_over_ours"] = round(e["us"] / per_kernel[ours]["us"], 3) if ours in per_kernel else None
+            out["cases"][name] = e
+        except Exception as ex:        # the library may lack the mode on a given ROCm
+            out["cases"][name] = {"unavailable": f"{type(ex).__name__}: {str(ex).splitlines()[0][:120]}"}
+    return out
 
 
 def _kernel_entry(us, work, kind):

@@ -40,10 +40,13 @@ def _out_host(c):
 
 
 @pytest.mark.parametrize("kind", ["fprop", "dgrad", "wgrad"])
-def test_pow2_exact_small_integer_problem(kind):
+@pytest.mark.parametrize("mnk", [(256, 384, 640), (256, 256, 128), (512, 512, 640), (256, 768, 1152)])
+def test_pow2_exact_small_integer_problem(kind, mnk):
+    """128x256 tiles (256, 384, 640) and 256x256 tiles: one K-group, and odd
+    K-group counts over several tiles."""
     fp8q = require_gpu()
-    rng = np.random.default_rng(131)
-    m, n, k = 256, 384, 640
+    rng = np.random.default_rng(131 + sum(mnk))
+    m, n, k = mnk
     ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50], np.uint8)   # 0,1..8
     def codes(shape):
         c = ints[rng.integers(0, ints.size, size=shape)]
@@ -168,6 +171,53 @@ def test_pow2_deterministic():
     c1 = host(fp8q.fp8_gemm_blockscaled_pow2(0, *args, out_dtype=torch.float32))
     c2 = host(fp8q.fp8_gemm_blockscaled_pow2(0, *args, out_dtype=torch.float32))
     assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------
+# Many 256x256 tiles, each checked on its own; FP32 plain and accumulating;
+# the tail of a grid split off as 128x256 tiles.
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,out,k", [("fprop", "bf16", 256), ("dgrad", "f32", 640), ("wgrad", "f32", 1152),
+                                         ("wgrad", "f32acc", 384), ("fprop", "f32acc", 128)])
+def test_pow2_many_tiles_every_tile(kind, out, k):
+    fp8q = require_gpu()
+    m = n = 2048                                   # 64 tiles of 256x256
+    ops = random_fp8_operands(401 + k, m, n, k, kind=kind, pow2=True)
+    ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind)
+    args = [dev(ops[x]) for x in ("qa", "sa", "qb", "sb")]
+    c0 = np.random.default_rng(402).standard_normal((m, n)).astype(np.float32)
+    outs = []
+    for _ in range(2):
+        if out == "f32acc":
+            c = dev(c0.copy())
+            fp8q.fp8_gemm_blockscaled_pow2(KINDS[kind], *args, c=c, accumulate=True)
+            got, want, tol = host(c).astype(np.float64), ref + c0.astype(np.float64), TOL_F32
+        else:
+            dt = torch.bfloat16 if out == "bf16" else torch.float32
+            c = fp8q.fp8_gemm_blockscaled_pow2(KINDS[kind], *args, out_dtype=dt)
+            got, want, tol = _out_host(c), og.round_output(ref, out), (TOL if out == "bf16" else TOL_F32)
+        outs.append(got)
+        for r0 in range(0, m, 256):
+            for c0_ in range(0, n, 256):
+                t = (slice(r0, r0 + 256), slice(c0_, c0_ + 256))
+                assert og.rel_frobenius(got[t], want[t]) <= tol, (r0, c0_)
+    assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("kind", ["fprop", "dgrad"])
+def test_pow2_tail_balanced_two_grid_launch(kind):
+    """M=512, N=129*256: 258 tiles of 256x256, so the last 256-column band runs
+    as a second grid of 128x256 tiles."""
+    fp8q = require_gpu()
+    m, n, k = 512, 129 * 256, 384
+    ops = random_fp8_operands(411, m, n, k, kind=kind, pow2=True)
+    ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind)
+    c = fp8q.fp8_gemm_blockscaled_pow2(KINDS[kind], *[dev(ops[x]) for x in ("qa", "sa", "qb", "sb")],
+                                       out_dtype=torch.bfloat16)
+    got, want = host_bf16_as_f64(c), og.round_bf16(ref)
+    for cols in (slice(0, 128 * 256), slice(128 * 256, n)):          # first grid, second grid
+        assert og.rel_frobenius(got[:, cols], want[:, cols]) <= TOL, cols
 
 
 @pytest.fixture(scope="module")
