@@ -33,7 +33,9 @@ shape and codes, with per-tensor and with MX scales (it offers no 1x128 /
 128x128 block scaling on ROCm), for context; not part of the step.
 
 cpu_baseline: the CPU oracle timed on this host on a bounded slice of every
-workload (per_config), with the host's core count and CPU model.
+workload (per_config), with the host's core count and CPU model; each line
+also records the parity of the timed GPU run on its slice (quantizer codes and
+scales bit for bit, GEMM outputs within the relative Frobenius bound).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--copy-calibration]
@@ -211,6 +213,18 @@ class Step:
         ]
         self.step_flop = sum(w for _, _, w, kind in self.kernels if kind == "flop")
 
+    def output_slices(self):
+        """Host copies of the step's outputs on the slices the CPU leg computes with the oracle (taken right after
+        the timed steps, before the outside-step kernels reuse the buffers)."""
+        h = lambda t: t.cpu().numpy()
+        starts = np.cumsum([0] + list(self.host["padded"][:3]))
+        rows = np.concatenate([np.arange(s0, s0 + 128) for s0 in starts])
+        return {"qx": h(self.qx[:2048]), "sx": h(self.sx[:, :2048]),
+                "qxt": h(self.qxt[:, :2048]), "sxt": h(self.sxt[:16]),
+                "qw": h(self.qw[:2048]), "sw": h(self.sw[:16]),
+                "y": h(self.y[:2048, :4096].float()), "dx": h(self.dx[:1024, :1024].float()),
+                "dw": h(self.dw[:1024, :1024]), "my": h(self.my[torch.from_numpy(rows).cuda()][:, :512].float())}
+
     def run(self, events=None):
         for i, (_, fn, _, _) in enumerate(self.kernels):
             if events is not None:
@@ -239,29 +253,52 @@ def host_slices(lin, dy, moe):
             "wt_in": np.ascontiguousarray(lin["wt"][:, :1024]), "dy": dy[:1024].copy(),
             "dy_t": np.ascontiguousarray(dy[:, :1024]), "x_t": np.ascontiguousarray(lin["x"][:, :1024]),
             "mx": moe["x"][rows], "mw": np.stack([moe["wt"][e * N_MOE:e * N_MOE + 512] for e in range(4)]),
-            "counts": np.asarray(moe["counts"][:4])}
+            "counts": np.asarray(moe["counts"][:4]), "padded": np.asarray(moe["padded"][:4])}
 
 
-def cpu_baseline(host):
+def cpu_baseline(host, gpu=None):
     """The oracle, as it stands, timed on this host's cores on a bounded slice of every workload.
 
     Operand preparation (widening, and the oracle's own quantization of the GEMM operand slices) is outside
     the timed parts; each GEMM line times the exact per-K-group product of its slice.  The headline value is the
-    Fprop slice's rate; every line is in per_config."""
+    Fprop slice's rate; every line is in per_config.  With `gpu` (the step's outputs on the same slices), every
+    line also records the parity of the timed GPU run on its slice: bit-exact codes and scales for the quantizers,
+    the relative Frobenius error against the oracle's product rounded to the output dtype for the GEMMs (bound
+    1e-3 for BF16, 2e-4 for FP32 outputs)."""
     from threadpoolctl import threadpool_info
     from oracle import gemm as og, quant as oq
     from workloads import bf16_bits_as_f32, tiny_fprop
     lines = []
 
-    def timed(fn):
-        t0 = time.perf_counter()
-        fn()
-        return time.perf_counter() - t0
+    out = {}
 
-    def add(config, kernel, secs, work, kind, sample):
+    def timed(fn, key=None):
+        t0 = time.perf_counter()
+        r = fn()
+        secs = time.perf_counter() - t0
+        if key is not None:
+            out[key] = r
+        return secs
+
+    def add(config, kernel, secs, work, kind, sample, parity=None):
         rate = work / secs / (1e12 if kind == "flop" else 1e9)
-        lines.append({"config": config, "kernel": kernel, "oracle_s": round(secs, 3),
-                      "rate": round(rate, 5), "unit": "TFLOP/s" if kind == "flop" else "GB/s", "sample": sample})
+        line = {"config": config, "kernel": kernel, "oracle_s": round(secs, 3),
+                "rate": round(rate, 5), "unit": "TFLOP/s" if kind == "flop" else "GB/s", "sample": sample}
+        if gpu is not None and parity is not None:
+            line["parity"] = parity()
+        lines.append(line)
+
+    def exact(*pairs):          # codes and scales, bit for bit
+        bad = 0
+        for g, o in pairs:
+            g8, o8 = np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(o).view(np.uint8)
+            bad += int(np.count_nonzero(g8 != o8)) if g8.shape == o8.shape else max(g8.size, o8.size)
+        return "bit-exact" if bad == 0 else f"MISMATCH: {bad} bytes differ"
+
+    def close(got, ref, out_dtype):
+        bound = 1e-3 if out_dtype == "bf16" else 2e-4
+        err = float(og.rel_frobenius(np.asarray(got, dtype=np.float64), og.round_output(ref, out_dtype)))
+        return {"rel_frobenius": float(f"{err:.3g}"), "bound": bound, "ok": err <= bound}
 
     # tiny Fprop: quantize both operands and multiply, whole problem
     d = tiny_fprop()
@@ -274,31 +311,36 @@ def cpu_baseline(host):
     # quantizer-only workload: 2048 of the 8192 activation rows, 2048 of the 18432 weight rows
     x = bf16_bits_as_f32(host["x"][:2048])
     qbytes = x.size * 2 + x.size + x.size // 128 * 4
-    add("quantizer-only", "quant_1x128 X (max-abs)", timed(lambda: oq.quant_1x128(x)), qbytes, "bytes",
-        "X rows 0..2047 of 8192")
-    add("quantizer-only", "quant_1x128 X (pow2)", timed(lambda: oq.quant_1x128(x, oq.MODE_POW2)), qbytes, "bytes",
-        "X rows 0..2047 of 8192")
-    add("quantizer-only", "quant_128x1 X (max-abs)", timed(lambda: oq.quant_128x1(x)), qbytes, "bytes",
-        "X rows 0..2047 of 8192")
+    add("quantizer-only", "quant_1x128 X (max-abs)", timed(lambda: oq.quant_1x128(x), "q1"), qbytes, "bytes",
+        "X rows 0..2047 of 8192", lambda: exact((gpu["qx"], out["q1"][0]), (gpu["sx"], out["q1"][1])))
+    add("quantizer-only", "quant_1x128 X (pow2)", timed(lambda: oq.quant_1x128(x, oq.MODE_POW2), "p1"), qbytes,
+        "bytes", "X rows 0..2047 of 8192",
+        lambda: exact((gpu["pow2_q"], out["p1"][0]), (gpu["pow2_s"], out["p1"][1])))
+    add("quantizer-only", "quant_128x1 X (max-abs)", timed(lambda: oq.quant_128x1(x), "t1"), qbytes, "bytes",
+        "X rows 0..2047 of 8192", lambda: exact((gpu["qxt"], out["t1"][0]), (gpu["sxt"], out["t1"][1])))
     w = bf16_bits_as_f32(host["wt"][:2048])
-    add("quantizer-only", "quant_128x128 W (max-abs)", timed(lambda: oq.quant_128x128(w)),
-        w.size * 3 + (w.size // 16384) * 4, "bytes", "W rows 0..2047 of 18432")
+    add("quantizer-only", "quant_128x128 W (max-abs)", timed(lambda: oq.quant_128x128(w), "b1"),
+        w.size * 3 + (w.size // 16384) * 4, "bytes", "W rows 0..2047 of 18432",
+        lambda: exact((gpu["qw"], out["b1"][0]), (gpu["sw"], out["b1"][1])))
     # Fprop: 2048 tokens x 4096 output channels, full K = 7168
     qa, sa = oq.quant_1x128(bf16_bits_as_f32(host["x"]))
     qb, sb = oq.quant_128x128(bf16_bits_as_f32(host["wt"]))
-    f_s = timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.FPROP))
+    f_s = timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.FPROP), "fprop")
     f_flop = 2.0 * qa.shape[0] * qb.shape[0] * D_IN
-    add("Fprop", "gemm Fprop", f_s, f_flop, "flop", f"M={qa.shape[0]} of 8192, N={qb.shape[0]} of 18432, K={D_IN}")
+    add("Fprop", "gemm Fprop", f_s, f_flop, "flop", f"M={qa.shape[0]} of 8192, N={qb.shape[0]} of 18432, K={D_IN}",
+        lambda: close(gpu["y"], out["fprop"], "bf16"))
     # Dgrad: 1024 tokens x 1024 input channels, full K = 18432
     qa, sa = oq.quant_1x128(bf16_bits_as_f32(host["dy"]))
     qb, sb = oq.quant_128x128(np.ascontiguousarray(bf16_bits_as_f32(host["wt_in"]).T))
-    add("Dgrad + Wgrad", "gemm Dgrad", timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.DGRAD)),
-        2.0 * qa.shape[0] * qb.shape[0] * D_OUT, "flop", f"M=1024 of 8192, N=1024 of 7168, K={D_OUT}")
+    add("Dgrad + Wgrad", "gemm Dgrad", timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.DGRAD), "dgrad"),
+        2.0 * qa.shape[0] * qb.shape[0] * D_OUT, "flop", f"M=1024 of 8192, N=1024 of 7168, K={D_OUT}",
+        lambda: close(gpu["dx"], out["dgrad"], "bf16"))
     # Wgrad: 1024 output x 1024 input channels, full K = 8192 tokens
     qa, sa = oq.quant_128x1(bf16_bits_as_f32(host["dy_t"]))
     qb, sb = oq.quant_128x1(bf16_bits_as_f32(host["x_t"]))
-    add("Dgrad + Wgrad", "gemm Wgrad", timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.WGRAD)),
-        2.0 * qa.shape[0] * qb.shape[0] * T, "flop", f"M=1024 of 18432, N=1024 of 7168, K={T}")
+    add("Dgrad + Wgrad", "gemm Wgrad", timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.WGRAD), "wgrad"),
+        2.0 * qa.shape[0] * qb.shape[0] * T, "flop", f"M=1024 of 18432, N=1024 of 7168, K={T}",
+        lambda: close(gpu["dw"], out["wgrad"], "f32"))
     # grouped: the first 128-row tile of experts 0..3, N = 512 of 2048 (real rows only in the FLOP count)
     qa, sa = oq.quant_1x128(bf16_bits_as_f32(host["mx"]))
     qbs = [oq.quant_128x128(bf16_bits_as_f32(wv)) for wv in host["mw"]]
@@ -306,8 +348,9 @@ def cpu_baseline(host):
     sb = np.stack([s_ for _, s_ in qbs])
     gmap = np.arange(4, dtype=np.int32)
     real = sum(min(128, int(c)) for c in host["counts"])
-    add("grouped MoE", "gemm grouped MoE", timed(lambda: og.grouped_ref(qa, sa, qb, sb, gmap)),
-        2.0 * real * 512 * D_IN, "flop", "first 128-row tile of experts 0..3, N=512 of 2048, K=7168")
+    add("grouped MoE", "gemm grouped MoE", timed(lambda: og.grouped_ref(qa, sa, qb, sb, gmap), "grouped"),
+        2.0 * real * 512 * D_IN, "flop", "first 128-row tile of experts 0..3, N=512 of 2048, K=7168",
+        lambda: close(gpu["my"], out["grouped"], "bf16"))
 
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     head = next(l for l in lines if l["kernel"] == "gemm Fprop")
@@ -351,6 +394,7 @@ def main():
     for i, (name, _, work, kind) in enumerate(step.kernels):
         us = float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)])) * 1e3
         per_kernel[name] = _kernel_entry(us, work, kind)
+    gpu_out = None if args.no_cpu_baseline else step.output_slices()
 
     # extra kernels outside the step, in order (power-of-two scale mode, FP8 re-tiling, hardware-scaled GEMMs).
     # Timed one call at a time, each preceded (outside its events) by a read of 512 MiB that evicts the
@@ -424,7 +468,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(step.host)
+        gpu_out["pow2_q"], gpu_out["pow2_s"] = step.pow2_q[:2048].cpu().numpy(), step.pow2_s[:, :2048].cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(step.host, gpu_out)
     print(json.dumps(result), flush=True)
 
 

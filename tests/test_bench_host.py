@@ -67,3 +67,50 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=300)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_cpu_baseline_records_the_parity_of_every_slice():
+    """The CPU leg compares the timed GPU run's outputs with the oracle on each slice it times: quantizers bit for
+    bit, GEMMs by relative Frobenius error against the stated bound.  Small synthetic slices (the leg takes its
+    shapes from them); the "GPU" outputs are the oracle's own, with one planted byte and one planted GEMM error."""
+    import numpy as np
+    from oracle import gemm as og, quant as oq
+    from workloads import bf16_bits_as_f32, to_bf16_bits
+    rng = np.random.default_rng(7)
+    b16 = lambda shape, sigma: to_bf16_bits((rng.standard_normal(shape) * sigma).astype(np.float32))
+    host = {"x": b16((256, 1024), 1.0), "wt": b16((512, 1024), 0.02), "wt_in": b16((512, 256), 0.02),
+            "dy": b16((256, 512), 1e-3), "dy_t": b16((256, 256), 1e-3), "x_t": b16((256, 256), 1.0),
+            "mx": b16((512, 1024), 1.0), "mw": b16((4, 512, 1024), 0.02),
+            "counts": np.array([100, 128, 50, 128]), "padded": np.array([128, 128, 128, 128])}
+    f = bf16_bits_as_f32
+    x = f(host["x"])
+    gpu = {}
+    gpu["qx"], gpu["sx"] = oq.quant_1x128(x)
+    gpu["pow2_q"], gpu["pow2_s"] = oq.quant_1x128(x, oq.MODE_POW2)
+    gpu["qxt"], gpu["sxt"] = oq.quant_128x1(x)
+    gpu["qw"], gpu["sw"] = oq.quant_128x128(f(host["wt"]))
+    qa, sa = gpu["qx"], gpu["sx"]
+    gpu["y"] = og.round_output(og.gemm_ref(qa, sa, gpu["qw"], gpu["sw"], og.FPROP), "bf16")
+    qa, sa = oq.quant_1x128(f(host["dy"]))
+    qb, sb = oq.quant_128x128(np.ascontiguousarray(f(host["wt_in"]).T))
+    gpu["dx"] = og.round_output(og.gemm_ref(qa, sa, qb, sb, og.DGRAD), "bf16")
+    qa, sa = oq.quant_128x1(f(host["dy_t"]))
+    qb, sb = oq.quant_128x1(f(host["x_t"]))
+    gpu["dw"] = og.round_output(og.gemm_ref(qa, sa, qb, sb, og.WGRAD), "f32")
+    qa, sa = oq.quant_1x128(f(host["mx"]))
+    qbs = [oq.quant_128x128(f(w)) for w in host["mw"]]
+    gpu["my"] = og.round_output(og.grouped_ref(qa, sa, np.stack([q for q, _ in qbs]), np.stack([s for _, s in qbs]),
+                                               np.arange(4, dtype=np.int32)), "bf16")
+    gpu["qxt"] = gpu["qxt"].copy()
+    gpu["qxt"][5, 7] ^= 1                                  # one planted code byte
+    gpu["dx"] = gpu["dx"] * 1.01                           # a planted 1% GEMM error
+    lines = {l["kernel"]: l for l in bench.cpu_baseline(host, gpu)["per_config"]}
+    assert lines["quant_1x128 X (max-abs)"]["parity"] == "bit-exact"
+    assert lines["quant_1x128 X (pow2)"]["parity"] == "bit-exact"
+    assert lines["quant_128x128 W (max-abs)"]["parity"] == "bit-exact"
+    assert lines["quant_128x1 X (max-abs)"]["parity"] == "MISMATCH: 1 bytes differ"
+    for k in ("gemm Fprop", "gemm Wgrad", "gemm grouped MoE"):
+        assert lines[k]["parity"]["ok"] and lines[k]["parity"]["rel_frobenius"] == 0.0, k
+    assert not lines["gemm Dgrad"]["parity"]["ok"]
+    assert lines["gemm Dgrad"]["parity"]["rel_frobenius"] > lines["gemm Dgrad"]["parity"]["bound"]
+    assert "parity" not in lines["quant 1x128 + 128x128 + Fprop (int64)"]     # the tiny case does not run on the GPU
