@@ -225,6 +225,19 @@ class Step:
                 "y": h(self.y[:2048, :4096].float()), "dx": h(self.dx[:1024, :1024].float()),
                 "dw": h(self.dw[:1024, :1024]), "my": h(self.my[torch.from_numpy(rows).cuda()][:, :512].float())}
 
+    def tiny_outputs(self):
+        """The tiny Fprop (128x256x128, FP32 in and out) through the library, for the CPU leg's parity record."""
+        from workloads import tiny_fprop
+        q = self.fp8q
+        d = tiny_fprop()
+        a = torch.from_numpy(d["a"]).cuda()
+        bt = torch.from_numpy(d["bt"]).cuda()
+        qa, sa = q.fp8_quant_tile(a, q.TILE_1x128, q.MAXABS)
+        qb, sb = q.fp8_quant_block(bt, q.MAXABS)
+        c = q.fp8_gemm_blockscaled(q.FPROP, qa, sa, qb, sb, out_dtype=torch.float32)
+        return {"tiny_qa": qa.cpu().numpy(), "tiny_sa": sa.cpu().numpy(), "tiny_qb": qb.cpu().numpy(),
+                "tiny_sb": sb.cpu().numpy(), "tiny_c": c.cpu().numpy()}
+
     def run(self, events=None):
         for i, (_, fn, _, _) in enumerate(self.kernels):
             if events is not None:
@@ -305,9 +318,14 @@ def cpu_baseline(host, gpu=None):
     def tiny():
         qa, sa = oq.quant_1x128(d["a"])
         qb, sb = oq.quant_128x128(d["bt"])
-        og.gemm_ref(qa, sa, qb, sb, og.FPROP, exact_int=True)
-    add("tiny Fprop 128x256x128", "quant 1x128 + 128x128 + Fprop (int64)", timed(tiny), 2.0 * 128 * 128 * 256, "flop",
-        "whole problem")
+        return qa, sa, qb, sb, og.gemm_ref(qa, sa, qb, sb, og.FPROP, exact_int=True)
+
+    def tiny_parity():
+        qa, sa, qb, sb, c = out["tiny"]
+        codes = exact((gpu["tiny_qa"], qa), (gpu["tiny_sa"], sa), (gpu["tiny_qb"], qb), (gpu["tiny_sb"], sb))
+        return {"codes_and_scales": codes, **close(gpu["tiny_c"], c, "f32")}
+    add("tiny Fprop 128x256x128", "quant 1x128 + 128x128 + Fprop (int64)", timed(tiny, "tiny"), 2.0 * 128 * 128 * 256,
+        "flop", "whole problem", tiny_parity)
     # quantizer-only workload: 2048 of the 8192 activation rows, 2048 of the 18432 weight rows
     x = bf16_bits_as_f32(host["x"][:2048])
     qbytes = x.size * 2 + x.size + x.size // 128 * 4
@@ -469,6 +487,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         gpu_out["pow2_q"], gpu_out["pow2_s"] = step.pow2_q[:2048].cpu().numpy(), step.pow2_s[:, :2048].cpu().numpy()
+        gpu_out.update(step.tiny_outputs())
         result["cpu_baseline"] = cpu_baseline(step.host, gpu_out)
     print(json.dumps(result), flush=True)
 

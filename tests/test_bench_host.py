@@ -101,6 +101,12 @@ def test_cpu_baseline_records_the_parity_of_every_slice():
     qbs = [oq.quant_128x128(f(w)) for w in host["mw"]]
     gpu["my"] = og.round_output(og.grouped_ref(qa, sa, np.stack([q for q, _ in qbs]), np.stack([s for _, s in qbs]),
                                                np.arange(4, dtype=np.int32)), "bf16")
+    from workloads import tiny_fprop
+    t = tiny_fprop()
+    gpu["tiny_qa"], gpu["tiny_sa"] = oq.quant_1x128(t["a"])
+    gpu["tiny_qb"], gpu["tiny_sb"] = oq.quant_128x128(t["bt"])
+    gpu["tiny_c"] = og.round_output(og.gemm_ref(gpu["tiny_qa"], gpu["tiny_sa"], gpu["tiny_qb"], gpu["tiny_sb"],
+                                                og.FPROP), "f32")
     gpu["qxt"] = gpu["qxt"].copy()
     gpu["qxt"][5, 7] ^= 1                                  # one planted code byte
     gpu["dx"] = gpu["dx"] * 1.01                           # a planted 1% GEMM error
@@ -113,4 +119,5 @@ def test_cpu_baseline_records_the_parity_of_every_slice():
         assert lines[k]["parity"]["ok"] and lines[k]["parity"]["rel_frobenius"] == 0.0, k
     assert not lines["gemm Dgrad"]["parity"]["ok"]
     assert lines["gemm Dgrad"]["parity"]["rel_frobenius"] > lines["gemm Dgrad"]["parity"]["bound"]
-    assert "parity" not in lines["quant 1x128 + 128x128 + Fprop (int64)"]     # the tiny case does not run on the GPU
+    tiny = lines["quant 1x128 + 128x128 + Fprop (int64)"]["parity"]
+    assert tiny["codes_and_scales"] == "bit-exact" and tiny["ok"] and tiny["rel_frobenius"] == 0.0
