@@ -196,8 +196,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   // the per-lane byte offset is a constant VGPR and the wave-uniform row and
   // K-group offset an SGPR, so the loop spends no VALU instruction on
   // addresses (with 64-bit global addresses it spent 12-18 per group; Fprop
-  // 2% faster).  The 32-bit offsets need 256 rows of A and B to span less
-  // than 2^31 bytes, which the C ABI checks (leading dimensions below 8 MiB).
+  // 2% faster).  The 32-bit offsets need a tile's rows of A and B (up to 512)
+  // to span less than 2^31 bytes, which the C ABI checks (leading dimensions
+  // below 4 MiB).
   // 0x00020000: the buffer descriptor's fourth word for untyped 32-bit
   // accesses on gfx9-family devices.
   const __amdgpu_buffer_rsrc_t rsrc_a =
@@ -267,10 +268,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   //    other);
   //  * fragment reads run ahead of their MFMAs: the group's A fragments and B
   //    fragments 0-1 up front, then B fragment bi+2 (with the per-column
-  //    Wgrad scales it needs) right after the first MFMA of block bi.  The
-  //    compiler only ever waits for all outstanding LDS reads (lgkmcnt(0)), so
-  //    every prefetch is issued right after an MFMA, never just before a
-  //    fragment's first use.
+  //    Wgrad scales it needs) right after the first MFMA of block bi, never
+  //    just before a fragment's first use: where the compiler cannot count
+  //    the LDS reads exactly (Wgrad, whose per-column scales come by a 64-bit
+  //    global DMA), it waits for all of them (lgkmcnt(0)) before a use.
   // A scheduling barrier after every step pins this interleave (left alone,
   // the compiler places each FMA right behind its own MFMA and pads the
   // hazard with s_nop).
