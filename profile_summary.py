@@ -5,8 +5,9 @@ JSON line lists its kernels in launch order (the step's kernels, then the
 ones timed outside the step, then the 1 GiB device copy), each call of the
 C ABI launches one grid, or two when a GEMM runs its last wave as a second
 grid of 128x256 tiles, and bench.py runs every step kernel (warm-up + timed
-steps) before the outside-step ones (2 untimed + timed calls each).  Each
-figure is the mean over the timed calls.
+steps) before the outside-step ones (2 untimed + timed calls each, and for a
+quantizer with a "warm" entry as many calls again back to back).  Each figure
+is the mean over the timed calls (for the outside-step ones, the cold calls).
 
   python profile_summary.py trace BENCH_JSON TRACE_DIR --steps K
       kernel-trace table (rocprofv3 --kernel-trace --stats) -> stdout (markdown)
@@ -109,7 +110,8 @@ def match(bench, disp, steps):
     fp8q = [d for d in disp if "fp8q::" in d["name"]]
     # the warm-up count is not needed: step calls come first, so the number of
     # step rounds is what remains after the outside-step calls
-    n_extra = sum(2 + steps for _ in extra_names)
+    warm = {n for n in extra_names if "warm" in kern[n]}     # these also ran `steps` calls back to back
+    n_extra = sum(2 + steps + (steps if n in warm else 0) for n in extra_names)
     calls = []          # consecutive calls, each a list of dispatches
     i = 0
     while i < len(fp8q):
@@ -128,12 +130,14 @@ def match(bench, disp, steps):
         raise ValueError(f"only {rounds} step rounds for --steps {steps}")
     seq = [n for _ in range(rounds) for n in step_names]
     for n in extra_names:
-        seq += [n] * (2 + steps)
+        seq += [n] * (2 + steps) + [(n, "warm")] * (steps if n in warm else 0)
     timed = {}
     for pos, (n, c) in enumerate(zip(seq, calls)):
-        if not any(f in c[0]["name"] for f in family(n)):
-            raise ValueError(f"call {pos} ({n}) matched dispatch {c[0]['name'][:80]}")
-        timed.setdefault(n, []).append(c)
+        base = n[0] if isinstance(n, tuple) else n
+        if not any(f in c[0]["name"] for f in family(base)):
+            raise ValueError(f"call {pos} ({base}) matched dispatch {c[0]['name'][:80]}")
+        if n == base:                   # the warm calls are matched but not summarised: the cold ones are timed
+            timed.setdefault(n, []).append(c)
     for n in timed:
         timed[n] = timed[n][-steps:]
     copies = [d for d in disp if "copy" in d["name"].lower()]

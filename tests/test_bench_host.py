@@ -117,6 +117,9 @@ def test_cpu_baseline_records_the_parity_of_every_slice():
     assert lines["quant_128x1 X (max-abs)"]["parity"] == "MISMATCH: 1 bytes differ"
     for k in ("gemm Fprop", "gemm Wgrad", "gemm grouped MoE"):
         assert lines[k]["parity"]["ok"] and lines[k]["parity"]["rel_frobenius"] == 0.0, k
+    # against the unrounded product: the output dtype's own rounding (BF16 about 1.7e-3, FP32 about 3e-8)
+    assert 1e-3 < lines["gemm Fprop"]["parity"]["rel_frobenius_raw"] < 3e-3
+    assert 0 < lines["gemm Wgrad"]["parity"]["rel_frobenius_raw"] < 1e-7
     assert not lines["gemm Dgrad"]["parity"]["ok"]
     assert lines["gemm Dgrad"]["parity"]["rel_frobenius"] > lines["gemm Dgrad"]["parity"]["bound"]
     tiny = lines["quant 1x128 + 128x128 + Fprop (int64)"]["parity"]

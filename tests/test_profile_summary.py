@@ -19,12 +19,17 @@ COPY = "__amd_rocclr_copyBuffer"
 BENCH = {"kernels": {
     "quant 1x128+128x1 X": {"us": 50.0},
     "gemm Dgrad": {"us": 900.0},
-    "quant_1x128 X (pow2 scales)": {"us": 30.0, "outside_step": True},
+    "quant_1x128 X (pow2 scales)": {"us": 30.0, "outside_step": True, "warm": {"us": 28.0}},
     ps.COPY: {"us": 400.0, "outside_step": True},
 }}
+# the same with an outside-step GEMM after the warm quantizer calls
+P2_NAME = "gemm Fprop (pow2 operands, hardware-scaled MFMA)"
+BENCH_P2 = {"kernels": {**{k: v for k, v in BENCH["kernels"].items() if k != ps.COPY},
+                        P2_NAME: {"us": 850.0, "outside_step": True}, ps.COPY: {"us": 400.0, "outside_step": True}}}
+GEMM_P2 = "void fp8q::gemm_blockscaled_kernel<256, 256, 4, 2, 0, 0, false, 3>(fp8q::GemmArgs)"
 
 
-def _rows(steps, warmup, counter):
+def _rows(steps, warmup, counter, p2_gemm=False):
     """Dispatch rows as the bench would launch them; each call's counter value encodes
     (kind, call index) so that the expected means are known."""
     rows, t = [], 0
@@ -45,6 +50,11 @@ def _rows(steps, warmup, counter):
     for c in range(2 + steps):
         add(REDUCE, 0.0)                      # the cache scrub between timed calls
         add(Q1, 50 + c)
+    for c in range(steps):
+        add(Q1, 90 + c)                       # the same quantizer back to back (warm)
+    for c in range(2 + steps if p2_gemm else 0):
+        add(REDUCE, 0.0)
+        add(GEMM_P2, 70 + c, dur=8000)
     for c in range(3 + 5):
         add(COPY, 524288.0 if counter == "FETCH_SIZE" else 1048576.0, dur=400000)
     return rows
@@ -57,6 +67,11 @@ def test_match_pairs_split_grids_and_keeps_the_timed_calls():
     assert [len(c) for c in timed["gemm Dgrad"]] == [2, 2]
     assert [c[0]["counters"]["FETCH_SIZE"] for c in timed["gemm Dgrad"]] == [1001, 1002]
     assert [c[0]["counters"]["FETCH_SIZE"] for c in timed["quant 1x128+128x1 X"]] == [101, 102]
+    assert [c[0]["counters"]["FETCH_SIZE"] for c in timed["quant_1x128 X (pow2 scales)"]] == [52, 53]   # cold
+    assert len(timed[ps.COPY]) == 5 and all(len(c) == 1 for c in timed[ps.COPY])
+    # an outside-step call after the warm ones is still matched to its own dispatches
+    timed, _ = ps.match(BENCH_P2, ps.dispatches(_rows(steps, warmup, "FETCH_SIZE", p2_gemm=True)), steps)
+    assert [c[0]["counters"]["FETCH_SIZE"] for c in timed[P2_NAME]] == [72, 73]
     assert [c[0]["counters"]["FETCH_SIZE"] for c in timed["quant_1x128 X (pow2 scales)"]] == [52, 53]
     assert len(timed[ps.COPY]) == 5 and all(len(c) == 1 for c in timed[ps.COPY])
 
