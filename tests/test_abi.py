@@ -200,3 +200,19 @@ def test_requant_validation():
     assert _requant(qt=A + 256) == fp8q.ERR_ALIAS          # codes out over codes in
     assert _requant(st=C + 1024) == fp8q.ERR_ALIAS         # scales out inside codes out
     assert _requant(st=B) == fp8q.ERR_ALIAS                # scales out over scales in
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """The binding has no CPU fallback: a package directory without libfp8q.so
+    refuses to import, naming the missing library."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "precision_fp8_quant_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "precision_fp8_quant_amd", "__init__.py"), pkg / "__init__.py")
+    res = subprocess.run([sys.executable, "-c", "import precision_fp8_quant_amd"], cwd=tmp_path,
+                         env={**os.environ, "PYTHONPATH": str(tmp_path)}, capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode != 0
+    assert "libfp8q.so is missing" in res.stderr and "no CPU fallback" in res.stderr
