@@ -63,3 +63,62 @@ def test_gemm_a_operand_beyond_2g_bytes():
     assert og.rel_frobenius(got, og.round_bf16(ref)) <= TOL
     del qa, qb, sa, sb, c
     torch.cuda.empty_cache()
+
+
+LD_MAX = (1 << 31) // 512 - 128          # the largest GEMM operand leading dimension the C ABI accepts (bytes)
+
+
+def _rows_at_max_ld(seed, rows, k):
+    """rows x k codes as a view with leading dimension LD_MAX; the rest of each row is NaN codes."""
+    buf = torch.full((rows, LD_MAX), 0x7F, dtype=torch.uint8, device="cuda")
+    buf[:, :k] = device_fp8_codes(seed, (rows, k))
+    return buf[:, :k]
+
+
+@pytest.mark.parametrize("kind,path", [("fprop", "promoted"), ("wgrad", "promoted"), ("dgrad", "pow2_ab"),
+                                       ("wgrad", "pow2_a")])
+def test_gemm_at_the_largest_leading_dimension(kind, path):
+    """A and B rows 4,194,176 bytes apart, the most the ABI accepts (a 256-row tile then spans 2^31 - 2^15 bytes
+    of 32-bit buffer offsets): every output against the oracle, and no NaN from the codes beyond K."""
+    fp8q = require_gpu()
+    kinds = {"fprop": fp8q.FPROP, "dgrad": fp8q.DGRAD, "wgrad": fp8q.WGRAD}
+    m = n = 256
+    k = 384
+    a = _rows_at_max_ld(321, m, k)
+    b = _rows_at_max_ld(322, n, k)
+    assert a.stride(0) == b.stride(0) == LD_MAX
+    rng = np.random.default_rng(323)
+    def scales(shape, pow2):                # exponents in [-12, -4), integral where the MFMA applies the scale
+        e = rng.uniform(-12, -4, size=shape)
+        return torch.from_numpy(np.exp2(np.floor(e) if pow2 else e).astype(np.float32)).cuda()
+    sa = scales((k // 128, m), path != "promoted")
+    sb = scales((k // 128, n) if kind == "wgrad" else (n // 128, k // 128), path == "pow2_ab")
+    if path == "promoted":
+        c = fp8q.fp8_gemm_blockscaled(kinds[kind], a, sa, b, sb, out_dtype=torch.float32)
+    else:
+        mask = fp8q.POW2_AB if path == "pow2_ab" else fp8q.POW2_A
+        c = fp8q.fp8_gemm_blockscaled_pow2(kinds[kind], a, sa, b, sb, out_dtype=torch.float32, pow2_operands=mask)
+    ref = og.gemm_ref(host(a.contiguous()), host(sa), host(b.contiguous()), host(sb), kind)
+    got = host(c).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= 2e-4
+    del a, b, c
+    torch.cuda.empty_cache()
+
+
+def test_grouped_at_the_largest_leading_dimension():
+    fp8q = require_gpu()
+    gmap = torch.tensor([1, 0], dtype=torch.int32, device="cuda")
+    m, n, k, groups = 256, 512, 256, 2
+    a = _rows_at_max_ld(331, m, k)
+    qb = device_fp8_codes(332, (groups, n, k))
+    rng = np.random.default_rng(333)
+    sa = torch.from_numpy(np.exp2(rng.uniform(-12, -4, size=(k // 128, m))).astype(np.float32)).cuda()
+    sb = torch.from_numpy(np.exp2(rng.uniform(-12, -4, size=(groups, n // 128, k // 128))).astype(np.float32)).cuda()
+    c = fp8q.fp8_gemm_blockscaled_grouped(gmap, a, sa, qb, sb, out_dtype=torch.float32)
+    ref = og.grouped_ref(host(a.contiguous()), host(sa), host(qb), host(sb), host(gmap))
+    got = host(c).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert og.rel_frobenius(got, og.round_output(ref, "f32")) <= 2e-4
+    del a, c
+    torch.cuda.empty_cache()
