@@ -30,8 +30,10 @@
  *     ABI does not depend on the size a C compiler picks for an enum; the
  *     FP8Q_* constants below are the valid values, anything else returns
  *     FP8Q_ERR_ARG.
- *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All work
- *     is enqueued on it; the library never synchronises.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream of the
+ *     calling thread's current device).  All work is enqueued on it and runs
+ *     on its device, so every pointer must be memory that device can access;
+ *     the library never synchronises.
  *   - Return value: an fp8q_status.  Arguments are validated before anything
  *     is launched; on the first violation the matching error is returned and
  *     nothing runs.  A launch failure returns FP8Q_ERR_HIP.  Device faults

@@ -87,10 +87,17 @@ def _check(status):
         raise Fp8qError(status)
 
 
-def _stream(stream):
-    if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+def _run(fn, dev, stream, *args):
+    """Call entry point `fn` with the tensors' device `dev` current and the stream resolved on it: the kernels run
+    on the stream's device, and the NULL stream (torch's default stream) is the current device's."""
+    if stream is not None and isinstance(getattr(stream, "device", None), torch.device) and stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
+    with torch.cuda.device(dev):
+        if stream is None:
+            handle = torch.cuda.current_stream(dev).cuda_stream
+        else:
+            handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        _check(fn(*args, handle))
 
 
 def _dtype_code(t):
@@ -157,8 +164,8 @@ def fp8_quant_tile(x, tile=TILE_1x128, mode=MAXABS, q=None, scales=None, stream=
         scales = torch.empty(s_shape, dtype=torch.float32, device=x.device)
     q = _expect(_codes(q), "q", torch.uint8, q_shape, x.device)
     _expect(scales, "scales", torch.float32, s_shape, x.device, dense=True)
-    _check(lib.fp8_quant_tile(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), tile, mode,
-                              q.data_ptr(), _ld(q), scales.data_ptr(), _stream(stream)))
+    _run(lib.fp8_quant_tile, x.device, stream, x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), tile, mode,
+         q.data_ptr(), _ld(q), scales.data_ptr())
     return q, scales
 
 
@@ -180,9 +187,8 @@ def fp8_quant_tile_dual(x, mode=MAXABS, q=None, scales=None, q_t=None, scales_t=
     _expect(scales, "scales", torch.float32, (_cdiv(cols, 128), rows), dev, dense=True)
     q_t = _expect(_codes(q_t), "q_t", torch.uint8, (cols, rows), dev)
     _expect(scales_t, "scales_t", torch.float32, (_cdiv(rows, 128), cols), dev, dense=True)
-    _check(lib.fp8_quant_tile_dual(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), mode,
-                                   q.data_ptr(), _ld(q), scales.data_ptr(), q_t.data_ptr(), _ld(q_t),
-                                   scales_t.data_ptr(), _stream(stream)))
+    _run(lib.fp8_quant_tile_dual, dev, stream, x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), mode,
+         q.data_ptr(), _ld(q), scales.data_ptr(), q_t.data_ptr(), _ld(q_t), scales_t.data_ptr())
     return q, scales, q_t, scales_t
 
 
@@ -213,9 +219,8 @@ def fp8_quant_block(w, mode=MAXABS, transposed=False, q=None, scales=None, q_t=N
     qt_ptr = q_t.data_ptr() if q_t is not None else None
     ld_qt = _ld(q_t) if q_t is not None else 0
     st_ptr = scales_t.data_ptr() if scales_t is not None else None
-    _check(lib.fp8_quant_block(w.data_ptr(), _dtype_code(w), rows, cols, _ld(w), mode,
-                               q.data_ptr(), _ld(q), scales.data_ptr(), qt_ptr, ld_qt, st_ptr,
-                               _stream(stream)))
+    _run(lib.fp8_quant_block, dev, stream, w.data_ptr(), _dtype_code(w), rows, cols, _ld(w), mode,
+         q.data_ptr(), _ld(q), scales.data_ptr(), qt_ptr, ld_qt, st_ptr)
     if transposed:
         return q, scales, q_t, scales_t
     return q, scales
@@ -252,8 +257,8 @@ def _gemm(fn, kind, a, a_scales, b, b_scales, out_dtype, c, accumulate, stream, 
     if c.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError(f"c must be bfloat16 or float32, got {c.dtype}")
     _expect(c, "c", c.dtype, (m, n), dev)
-    _check(fn(kind, m, n, k, a.data_ptr(), _ld(a), a_scales.data_ptr(), b.data_ptr(), _ld(b), b_scales.data_ptr(),
-              c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0, *extra, _stream(stream)))
+    _run(fn, dev, stream, kind, m, n, k, a.data_ptr(), _ld(a), a_scales.data_ptr(), b.data_ptr(), _ld(b),
+         b_scales.data_ptr(), c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0, *extra)
     return c
 
 
@@ -279,9 +284,8 @@ def fp8_gemm_blockscaled_grouped(group_of_mtile, a, a_scales, b, b_scales, out_d
     if c.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError(f"c must be bfloat16 or float32, got {c.dtype}")
     _expect(c, "c", c.dtype, (m, n), dev)
-    _check(lib.fp8_gemm_blockscaled_grouped(g, m, n, k, group_of_mtile.data_ptr(), a.data_ptr(), _ld(a),
-                                            a_scales.data_ptr(), b.data_ptr(), b_scales.data_ptr(),
-                                            c.data_ptr(), _dtype_code(c), _ld(c), _stream(stream)))
+    _run(lib.fp8_gemm_blockscaled_grouped, dev, stream, g, m, n, k, group_of_mtile.data_ptr(), a.data_ptr(),
+         _ld(a), a_scales.data_ptr(), b.data_ptr(), b_scales.data_ptr(), c.data_ptr(), _dtype_code(c), _ld(c))
     return c
 
 
@@ -298,6 +302,6 @@ def fp8_requant_1x128_to_128x1(q, scales, mode=POW2, q_t=None, scales_t=None, st
         scales_t = torch.empty((_cdiv(rows, 128), cols), dtype=torch.float32, device=dev)
     q_t = _expect(_codes(q_t), "q_t", torch.uint8, (cols, rows), dev)
     _expect(scales_t, "scales_t", torch.float32, (_cdiv(rows, 128), cols), dev, dense=True)
-    _check(lib.fp8_requant_1x128_to_128x1(q.data_ptr(), rows, cols, _ld(q), scales.data_ptr(), mode,
-                                          q_t.data_ptr(), _ld(q_t), scales_t.data_ptr(), _stream(stream)))
+    _run(lib.fp8_requant_1x128_to_128x1, dev, stream, q.data_ptr(), rows, cols, _ld(q), scales.data_ptr(), mode,
+         q_t.data_ptr(), _ld(q_t), scales_t.data_ptr())
     return q_t, scales_t

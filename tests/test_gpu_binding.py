@@ -97,3 +97,21 @@ def test_grouped_operands_checked():
         fp8q.fp8_gemm_blockscaled_grouped(gmap, a, sa, b, _t((g, n // 128 + 1, k // 128), F32))
     with pytest.raises(ValueError, match="c has shape"):
         fp8q.fp8_gemm_blockscaled_grouped(gmap, a, sa, b, sb, c=_t((m - 128, n), BF))
+
+
+def test_stream_on_another_device_is_rejected():
+    """Kernels run on the stream's device: a stream object that names another
+    device than the tensors' is refused before anything is launched."""
+    import types
+    fp8q = require_gpu()
+    x = _t((128, 128), BF)
+    other = types.SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=0)
+    with pytest.raises(ValueError, match="stream is on"):
+        fp8q.fp8_quant_tile(x, fp8q.TILE_1x128, fp8q.MAXABS, stream=other)
+    # the tensors' own device: accepted, on an explicit stream and on the default one
+    s = torch.cuda.Stream()
+    q, sc = fp8q.fp8_quant_tile(x, fp8q.TILE_1x128, fp8q.MAXABS, stream=s)
+    s.synchronize()
+    q2, sc2 = fp8q.fp8_quant_tile(x, fp8q.TILE_1x128, fp8q.MAXABS)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(sc, sc2)
