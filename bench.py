@@ -271,7 +271,8 @@ def host_slices(lin, dy, moe):
 
 
 def cpu_baseline(host, gpu=None):
-    """The oracle, as it stands, timed on this host's cores on a bounded slice of every workload.
+    """The oracle, as it stands, timed on this host's cores on a bounded slice of every workload (the median of 3
+    runs for the tiny problem and the quantizer slices, one run for each GEMM slice).
 
     Operand preparation (widening, and the oracle's own quantization of the GEMM operand slices) is outside
     the timed parts; each GEMM line times the exact per-K-group product of its slice.  The headline value is the
@@ -286,13 +287,16 @@ def cpu_baseline(host, gpu=None):
 
     out = {}
 
-    def timed(fn, key=None):
-        t0 = time.perf_counter()
-        r = fn()
-        secs = time.perf_counter() - t0
+    def timed(fn, key=None, runs=1):
+        # the median of `runs` timings (3 for the tiny and quantizer slices, 1 for the GEMM slices)
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            r = fn()
+            ts.append(time.perf_counter() - t0)
         if key is not None:
             out[key] = r
-        return secs
+        return float(np.median(ts))
 
     def add(config, kernel, secs, work, kind, sample, parity=None):
         rate = work / secs / (1e12 if kind == "flop" else 1e9)
@@ -330,20 +334,20 @@ def cpu_baseline(host, gpu=None):
         qa, sa, qb, sb, c = out["tiny"]
         codes = exact((gpu["tiny_qa"], qa), (gpu["tiny_sa"], sa), (gpu["tiny_qb"], qb), (gpu["tiny_sb"], sb))
         return {"codes_and_scales": codes, **close(gpu["tiny_c"], c, "f32")}
-    add("tiny Fprop 128x256x128", "quant 1x128 + 128x128 + Fprop (int64)", timed(tiny, "tiny"), 2.0 * 128 * 128 * 256,
-        "flop", "whole problem", tiny_parity)
+    add("tiny Fprop 128x256x128", "quant 1x128 + 128x128 + Fprop (int64)", timed(tiny, "tiny", runs=3),
+        2.0 * 128 * 128 * 256, "flop", "whole problem", tiny_parity)
     # quantizer-only workload: 2048 of the 8192 activation rows, 2048 of the 18432 weight rows
     x = bf16_bits_as_f32(host["x"][:2048])
     qbytes = x.size * 2 + x.size + x.size // 128 * 4
-    add("quantizer-only", "quant_1x128 X (max-abs)", timed(lambda: oq.quant_1x128(x), "q1"), qbytes, "bytes",
+    add("quantizer-only", "quant_1x128 X (max-abs)", timed(lambda: oq.quant_1x128(x), "q1", runs=3), qbytes, "bytes",
         "X rows 0..2047 of 8192", lambda: exact((gpu["qx"], out["q1"][0]), (gpu["sx"], out["q1"][1])))
-    add("quantizer-only", "quant_1x128 X (pow2)", timed(lambda: oq.quant_1x128(x, oq.MODE_POW2), "p1"), qbytes,
+    add("quantizer-only", "quant_1x128 X (pow2)", timed(lambda: oq.quant_1x128(x, oq.MODE_POW2), "p1", runs=3), qbytes,
         "bytes", "X rows 0..2047 of 8192",
         lambda: exact((gpu["pow2_q"], out["p1"][0]), (gpu["pow2_s"], out["p1"][1])))
-    add("quantizer-only", "quant_128x1 X (max-abs)", timed(lambda: oq.quant_128x1(x), "t1"), qbytes, "bytes",
+    add("quantizer-only", "quant_128x1 X (max-abs)", timed(lambda: oq.quant_128x1(x), "t1", runs=3), qbytes, "bytes",
         "X rows 0..2047 of 8192", lambda: exact((gpu["qxt"], out["t1"][0]), (gpu["sxt"], out["t1"][1])))
     w = bf16_bits_as_f32(host["wt"][:2048])
-    add("quantizer-only", "quant_128x128 W (max-abs)", timed(lambda: oq.quant_128x128(w), "b1"),
+    add("quantizer-only", "quant_128x128 W (max-abs)", timed(lambda: oq.quant_128x128(w), "b1", runs=3),
         w.size * 3 + (w.size // 16384) * 4, "bytes", "W rows 0..2047 of 18432",
         lambda: exact((gpu["qw"], out["b1"][0]), (gpu["sw"], out["b1"][1])))
     # Fprop: 2048 tokens x 4096 output channels, full K = 7168
