@@ -26,6 +26,8 @@ Cases:
     varies from 2^-40 to 2^40 between cases.  Bar: bit-exact codes and scales.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -44,10 +46,12 @@ PATHS = {"promoted": 0, "pow2_a": 1, "pow2_b": 2, "pow2_ab": 3}
 NAN_CODE = 0x7F
 CODE_SENTINEL = 0xA5
 OUT_SENTINEL = -7.5              # exact in BF16 and FP32
+# FP8Q_GENERATED_ROUNDS=R draws R rounds of cases (round r from seeds shifted by r): a wider sweep on demand
+ROUNDS = int(os.environ.get("FP8Q_GENERATED_ROUNDS", "1"))
 
 
-def _draw_gemm_cases(n):
-    rng = np.random.default_rng(20261203)
+def _draw_gemm_cases(n, rnd=0):
+    rng = np.random.default_rng(20261203 + 7919 * rnd)
     cases = []
     for i in range(n):
         kind = ["fprop", "dgrad", "wgrad"][i % 3]
@@ -57,11 +61,11 @@ def _draw_gemm_cases(n):
         k = 128 * int(rng.integers(1, 11))
         pads = tuple(16 * int(v) for v in rng.integers(0, 3, size=4))      # A offset, A pad, B offset, B pad
         cpad = tuple(int(v) for v in rng.integers(0, 3, size=2))           # C offset, pad in 16-byte units
-        cases.append((i, kind, path, out, m, nn, k, pads, cpad))
+        cases.append((1000 * rnd + i, kind, path, out, m, nn, k, pads, cpad))
     return cases
 
 
-GEMM_CASES = _draw_gemm_cases(48)
+GEMM_CASES = [c for r in range(ROUNDS) for c in _draw_gemm_cases(48, r)]
 
 
 def _case_id(c):
@@ -186,8 +190,8 @@ def test_generated_gemm(case):
             assert err <= TOL_F32, (r, cc, err)
 
 
-def _draw_grouped_cases():
-    rng = np.random.default_rng(20261204)
+def _draw_grouped_cases(rnd=0):
+    rng = np.random.default_rng(20261204 + 7919 * rnd)
     cases = []
     for i, n in enumerate([128, 384, 256, 768, 512, 2048, 640, 1536, 1024, 896]):
         g = int(rng.integers(1, 6))
@@ -201,11 +205,12 @@ def _draw_grouped_cases():
         gmap[skip[0]] = -1
         gmap[skip[1]] = g                                    # both out of range
         out = ["bf16", "f32"][i % 2]
-        cases.append((i, n, g, k, gmap, out, 16 * int(rng.integers(0, 3)), 16 * int(rng.integers(0, 3))))
+        cases.append((1000 * rnd + i, n, g, k, gmap, out, 16 * int(rng.integers(0, 3)),
+                      16 * int(rng.integers(0, 3))))
     return cases
 
 
-GROUPED_CASES = _draw_grouped_cases()
+GROUPED_CASES = [c for r in range(ROUNDS) for c in _draw_grouped_cases(r)]
 
 
 @pytest.mark.parametrize("case", GROUPED_CASES, ids=lambda c: f"{c[0]}-n{c[1]}-g{c[2]}-k{c[3]}-{c[5]}")
@@ -262,8 +267,8 @@ def test_generated_grouped(case):
 # Quantizers
 # ----------------------------------------------------------------------------
 
-def _draw_quant_cases():
-    rng = np.random.default_rng(20261205)
+def _draw_quant_cases(rnd=0):
+    rng = np.random.default_rng(20261205 + 7919 * rnd)
     cases = []
     ops = ["1x128", "128x1", "dual", "block", "block_t", "requant"]
     for i in range(48):
@@ -280,11 +285,11 @@ def _draw_quant_cases():
             cols = 256 * int(rng.integers(1, 5))            # the two-block kernel for BF16 weights
         expo = int(rng.integers(-40, 41))
         offs = tuple(int(v) for v in rng.integers(0, 3, size=4))  # x offset, x pad, out offset, out pad (16 B)
-        cases.append((i, op, dtype, mode, rows, cols, expo, offs))
+        cases.append((1000 * rnd + i, op, dtype, mode, rows, cols, expo, offs))
     return cases
 
 
-QUANT_CASES = _draw_quant_cases()
+QUANT_CASES = [c for r in range(ROUNDS) for c in _draw_quant_cases(r)]
 MODE_CODE = {"maxabs": 0, "pow2": 1}
 
 
