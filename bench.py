@@ -223,7 +223,7 @@ class Step:
         return {"qx": h(self.qx[:2048]), "sx": h(self.sx[:, :2048]),
                 "qxt": h(self.qxt[:, :2048]), "sxt": h(self.sxt[:16]),
                 "qw": h(self.qw[:2048]), "sw": h(self.sw[:16]),
-                "y": h(self.y[:2048, :4096].float()), "dx": h(self.dx[:1024, :1024].float()),
+                "y": h(self.y[:2048, :4096].float()), "dx": h(self.dx[:1024, D_IN - 1024:].float()),
                 "dw": h(self.dw[:1024, :1024]), "my": h(self.my[torch.from_numpy(rows).cuda()][:, :512].float())}
 
     def tiny_outputs(self):
@@ -264,7 +264,7 @@ def host_slices(lin, dy, moe):
     starts = np.concatenate([[0], np.cumsum(moe["padded"])])[:4]
     rows = np.concatenate([np.arange(s0, s0 + 128) for s0 in starts])
     return {"x": lin["x"][:2048].copy(), "wt": lin["wt"][:4096].copy(),
-            "wt_in": np.ascontiguousarray(lin["wt"][:, :1024]), "dy": dy[:1024].copy(),
+            "wt_in": np.ascontiguousarray(lin["wt"][:, D_IN - 1024:]), "dy": dy[:1024].copy(),
             "dy_t": np.ascontiguousarray(dy[:, :1024]), "x_t": np.ascontiguousarray(lin["x"][:, :1024]),
             "mx": moe["x"][rows], "mw": np.stack([moe["wt"][e * N_MOE:e * N_MOE + 512] for e in range(4)]),
             "counts": np.asarray(moe["counts"][:4]), "padded": np.asarray(moe["padded"][:4])}
@@ -357,11 +357,12 @@ def cpu_baseline(host, gpu=None):
     f_flop = 2.0 * qa.shape[0] * qb.shape[0] * D_IN
     add("Fprop", "gemm Fprop", f_s, f_flop, "flop", f"M={qa.shape[0]} of 8192, N={qb.shape[0]} of 18432, K={D_IN}",
         lambda: close(gpu["y"], out["fprop"], "bf16"))
-    # Dgrad: 1024 tokens x 1024 input channels, full K = 18432
+    # Dgrad: 1024 tokens x the last 1024 input channels (the columns whose tiles run in the last wave, with K
+    # split in two), full K = 18432
     qa, sa = oq.quant_1x128(bf16_bits_as_f32(host["dy"]))
     qb, sb = oq.quant_128x128(np.ascontiguousarray(bf16_bits_as_f32(host["wt_in"]).T))
     add("Dgrad + Wgrad", "gemm Dgrad", timed(lambda: og.gemm_ref(qa, sa, qb, sb, og.DGRAD), "dgrad"),
-        2.0 * qa.shape[0] * qb.shape[0] * D_OUT, "flop", f"M=1024 of 8192, N=1024 of 7168, K={D_OUT}",
+        2.0 * qa.shape[0] * qb.shape[0] * D_OUT, "flop", f"M=1024 of 8192, N=1024 of 7168 (input channels 6144..7167), K={D_OUT}",
         lambda: close(gpu["dx"], out["dgrad"], "bf16"))
     # Wgrad: 1024 output x 1024 input channels, full K = 8192 tokens
     qa, sa = oq.quant_128x1(bf16_bits_as_f32(host["dy_t"]))

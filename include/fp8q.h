@@ -180,7 +180,11 @@ int fp8_quant_tile_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, 
  *            DGRAD  -- dX = dY W^T: A = dY quantized 1x128, B = W's transposed copy.
  *            WGRAD  -- dW = dY^T X: A = dY^T (128x1, transposed), B = X^T (128x1, transposed).
  * c        : C[M][N], leading dimension ldc (elements), dtype c_dtype
- *            (FP8Q_BF16, rounded to nearest-even, or FP8Q_F32).
+ *            (FP8Q_BF16, rounded to nearest-even, or FP8Q_F32).  With BF16
+ *            output the call may use C's own rows as temporary FP32 storage
+ *            before writing the result there (C is an output: nothing the
+ *            caller put in it is read); only the columns [0, N) of C are ever
+ *            touched, and C holds the result once the call's work completes.
  * accumulate : 0 -> C = result; 1 -> C += result (FP8Q_F32 output only).
  * Requires M, N, K multiples of 128, and lda, ldb of at most 4,194,176 bytes
  * (the kernels address a tile's rows with 32-bit offsets); otherwise

@@ -60,6 +60,9 @@ struct GemmArgs {
   // leading dimension of the A scales [K/128][sa_ld] (the full M; a grid
   // that covers a band of rows gets sa offset to its first row)
   int64_t sa_ld;
+  // K-split grids (KSPLIT > 1, FP32 output): elements between the output
+  // matrices of consecutive K ranges
+  int64_t split_c_off;
 };
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -101,7 +104,10 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lq) {
   return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
 }
 
-template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, int HW>
+// KSPLIT > 1: every tile is computed KSPLIT times, each over its share of the
+// K-groups, into its own FP32 output (p.c + part * p.split_c_off); a second
+// kernel adds the parts.
+template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, int HW, int KSPLIT = 1>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM;          // wave tile rows (M)
@@ -134,9 +140,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   const int wn = wave % WN;
 
   // ---- tile scheduling: XCD-aware remap, then grouped-M ordering ----------
+  static_assert(KSPLIT == 1 || (OUT == kOutF32 && !GROUPED), "K-split grids write FP32 parts");
   const int64_t tiles_m = p.M / BM;
   const int64_t tiles_n = p.N / BN;
-  const int64_t ntiles = tiles_m * tiles_n;
+  const int64_t ntiles = tiles_m * tiles_n * KSPLIT;    // with K split: (tile, part) pairs, parts adjacent
   // Workgroup i runs on XCD i % 8.  Plain GEMMs: give every XCD one
   // contiguous range of tiles (ceil or floor of ntiles/8), so neighbouring
   // tiles share its L2.  Grouped GEMMs: deal the 32-tile runs of the
@@ -158,6 +165,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     const int64_t q = ntiles >> 3, r = ntiles & 7, x = bid & 7, l = bid >> 3;
     bid = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + l;
   }
+  const int part = KSPLIT > 1 ? int(bid % KSPLIT) : 0;
+  if constexpr (KSPLIT > 1) bid /= KSPLIT;
   constexpr int64_t GROUP_M = 8;
   const int64_t per_group = GROUP_M * tiles_n;
   const int64_t first_m = (bid / per_group) * GROUP_M;
@@ -175,7 +184,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
     bptr += int64_t(grp) * p.b_group_stride;
     sbptr += int64_t(grp) * p.sb_group_stride;
   }
-  const int64_t KG = p.K >> 7;
+  const int64_t KG = p.K >> 7;                 // K-groups of the whole problem (scale indexing)
+  const int64_t kg0 = KSPLIT > 1 ? (KG * part) / KSPLIT : 0;          // this block's range of them
+  const int64_t kg1 = KSPLIT > 1 ? (KG * (part + 1)) / KSPLIT : KG;
 
   // ---- DMA addressing ------------------------------------------------------
   // Wave-wide DMA instruction `blk` fills LDS rows 8*blk .. 8*blk+7; lane l
@@ -293,12 +304,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
 
   float sa_cur[SM], sa_nxt[SM];
   float sb_cur = 0.0f, sb_nxt = 0.0f;
-  if (KG > 0) {
-    issue_stage(0, 0);
-    issue_scales(0, 0);
+  if (kg1 > kg0) {
+    issue_stage(kg0, 0);
+    issue_scales(kg0, 0);
 #pragma unroll
-    for (int ms = 0; ms < SM; ++ms) sa_cur[ms] = p.sa[m_lane + 16 * ms];
-    if constexpr (BSCALE == kScaleBlock) sb_cur = sbptr[(n_wave >> 7) * KG];
+    for (int ms = 0; ms < SM; ++ms) sa_cur[ms] = p.sa[kg0 * p.sa_ld + m_lane + 16 * ms];
+    if constexpr (BSCALE == kScaleBlock) sb_cur = sbptr[(n_wave >> 7) * KG + kg0];
     wait_vmem_all();
   }
   __syncthreads();
@@ -306,9 +317,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
   // One basic block per iteration (no branches between the MFMAs and their
   // promotion FMAs): the last iteration simply re-fetches its own group into
   // the idle stage, which nobody reads.
-  for (int64_t g = 0; g < KG; ++g) {
-    const int stage = int(g & 1);
-    const int64_t gn = g + 1 < KG ? g + 1 : g;
+  for (int64_t g = kg0; g < kg1; ++g) {
+    const int stage = int((g - kg0) & 1);
+    const int64_t gn = g + 1 < kg1 ? g + 1 : g;
     issue_scales(gn, stage ^ 1);
 #pragma unroll
     for (int ms = 0; ms < SM; ++ms) sa_nxt[ms] = p.sa[gn * p.sa_ld + m_lane + 16 * ms];
@@ -474,7 +485,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
       if constexpr (OUT == kOutBF16) {
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.c) + m * p.ldc + n));
       } else {
-        v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.c) + m * p.ldc + n);
+        float* const c = static_cast<float*>(p.c) + (KSPLIT > 1 ? part * p.split_c_off : 0);
+        v4f* dst = reinterpret_cast<v4f*>(c + m * p.ldc + n);
         v4f o = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
         if constexpr (OUT == kOutF32Acc) o += *dst;
         __builtin_nontemporal_store(o, dst);
@@ -486,14 +498,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_blockscaled_kernel(GemmArgs
 // ---------------------------------------------------------------------------
 // Launch configurations.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, int HW>
+template <int BM, int BN, int WM, int WN, int BSCALE, int OUT, bool GROUPED, int HW, int KSPLIT = 1>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
-  const int64_t tiles = (a.M / BM) * (a.N / BN);
+  const int64_t tiles = (a.M / BM) * (a.N / BN) * KSPLIT;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WM, WN, BSCALE, OUT, GROUPED, HW>),
+  hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WM, WN, BSCALE, OUT, GROUPED, HW, KSPLIT>),
                      dim3(unsigned(tiles)), dim3(WM * WN * 64), 0, st, a);
   return hipGetLastError();
 }
+
+namespace {
+// The BF16 columns of a GEMM whose K was split in two:
+//   c[m][n] = RNE(p[m][n] + p[m][half + n]),  n < cols,
+// p holding the two FP32 parts side by side in rows of ldp floats.  Eight
+// columns per thread (cols % 8 == 0), 16-byte loads and stores.
+__global__ __launch_bounds__(256) void ksplit_sum_bf16_kernel(const float* __restrict__ p, int64_t ldp, int64_t half,
+                                                              uint16_t* __restrict__ c, int64_t ldc, int64_t rows,
+                                                              int64_t cols) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= rows * cols) return;
+  const int64_t m = i / cols, n = i % cols;
+  const v4f* a = reinterpret_cast<const v4f*>(p + m * ldp + n);
+  const v4f* b = reinterpret_cast<const v4f*>(p + m * ldp + half + n);
+  const v4f lo = a[0] + b[0], hi = a[1] + b[1];
+  const u32x4 w = {bf16_rne_bits(lo[0]) | (bf16_rne_bits(lo[1]) << 16), bf16_rne_bits(lo[2]) | (bf16_rne_bits(lo[3]) << 16),
+                   bf16_rne_bits(hi[0]) | (bf16_rne_bits(hi[1]) << 16), bf16_rne_bits(hi[2]) | (bf16_rne_bits(hi[3]) << 16)};
+  *reinterpret_cast<u32x4*>(c + m * ldc + n) = w;
+}
+}  // namespace
 
 // Tile configurations, largest that divides the problem:
 //   256x256, 8 waves (4 along M x 2 along N) of 64x128
@@ -558,6 +590,29 @@ static hipError_t launch_balanced(const GemmArgs& a, hipStream_t st) {
         rest.b = a.b + head.N * a.ldb;
         rest.sb = a.sb + (head.N / 128) * (a.K / 128);
         rest.c = static_cast<uint8_t*>(a.c) + head.N * (OUT == kOutBF16 ? 2 : 4);
+        // BF16 output with room for two FP32 copies of the tail in the head
+        // columns of C (which the head grid writes afterwards): the tail runs
+        // as whole 256x256 tiles, each as two K halves in one wave of
+        // 2 x tail workgroups, into that scratch, and a third kernel adds the
+        // halves into the tail columns.  Otherwise the tail bands run as
+        // 128x256 tiles over the whole K, which read more LDS bytes per MFMA.
+        if constexpr (OUT == kOutBF16) {
+          if (a.K >= 256 && head.N >= 4 * rest.N) {
+            GemmArgs part = rest;
+            part.c = a.c;                        // FP32 rows of ldc / 2 floats over C's head columns
+            part.ldc = a.ldc / 2;
+            part.split_c_off = rest.N;
+            hipError_t e = launch_cfg<256, 256, 4, 2, BSCALE, kOutF32, false, HW, 2>(part, st);
+            if (e != hipSuccess) return e;
+            const int64_t threads = a.M * rest.N / 8;
+            hipLaunchKernelGGL(ksplit_sum_bf16_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, st,
+                               static_cast<const float*>(a.c), a.ldc / 2, rest.N, static_cast<uint16_t*>(rest.c),
+                               a.ldc, a.M, rest.N);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_cfg<256, 256, 4, 2, BSCALE, OUT, false, HW>(head, st);
+          }
+        }
         const hipError_t e = launch_cfg<256, 256, 4, 2, BSCALE, OUT, false, HW>(head, st);
         if (e != hipSuccess) return e;
         return launch_cfg<128, 256, 2, 4, BSCALE, OUT, false, HW>(rest, st);

@@ -4,7 +4,9 @@ Every bench call is matched to its GPU dispatches by position: the bench's
 JSON line lists its kernels in launch order (the step's kernels, then the
 ones timed outside the step, then the 1 GiB device copy), each call of the
 C ABI launches one grid, or two when a GEMM runs its last wave as a second
-grid of 128x256 tiles, and bench.py runs every step kernel (warm-up + timed
+grid of 128x256 tiles, or three when a BF16 GEMM runs its last wave with K
+split in two (the split grid, the kernel adding the halves, the grid of the
+other columns), and bench.py runs every step kernel (warm-up + timed
 steps) before the outside-step ones (2 untimed + timed calls each, and for a
 quantizer with a "warm" entry as many calls again back to back).  Each figure
 is the mean over the timed calls (for the outside-step ones, the cold calls).
@@ -74,6 +76,20 @@ def is_second_grid(kernel_name):
     return "gemm_blockscaled_kernel<128, 256, 2, 4," in kernel_name
 
 
+def continues_call(call, kernel_name):
+    """Whether a dispatch belongs to the GEMM call whose dispatches so far are `call`: the 128x256 grid of a
+    balanced last wave, or, for a BF16 call whose last wave ran with K split in two, the kernel that adds the two
+    halves and then the grid of the remaining columns."""
+    first, last = call[0]["name"], call[-1]["name"]
+    if "gemm_blockscaled_kernel" not in first:
+        return False
+    if is_second_grid(kernel_name):
+        return True
+    if "ksplit_sum_bf16_kernel" in kernel_name:
+        return "gemm_blockscaled_kernel" in last and len(call) == 1
+    return "ksplit_sum_bf16_kernel" in last and "gemm_blockscaled_kernel" in kernel_name
+
+
 def read_bench(path):
     with open(path) as fh:
         for line in fh:
@@ -117,7 +133,7 @@ def match(bench, disp, steps):
     while i < len(fp8q):
         c = [fp8q[i]]
         i += 1
-        while i < len(fp8q) and is_second_grid(fp8q[i]["name"]) and "gemm" in c[0]["name"]:
+        while i < len(fp8q) and continues_call(c, fp8q[i]["name"]):
             c.append(fp8q[i])
             i += 1
         calls.append(c)

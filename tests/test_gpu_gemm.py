@@ -99,6 +99,52 @@ def test_tail_balanced_two_grid_launch(kind, out):
         assert og.rel_frobenius(got[:, cols], want[:, cols]) <= tol, cols
 
 
+@pytest.mark.parametrize("path,k", [("promoted", 640), ("promoted", 256), ("pow2_a", 384), ("pow2_b", 640),
+                                    ("pow2_ab", 1152)])
+def test_ksplit_tail_into_the_head_columns(path, k):
+    """BF16 output whose last wave is at most half full: M=512, N=129*256 has 258 tiles of 256x256, so the two
+    tiles of the last 256-column band run as four workgroups, each tile as two K halves (KG odd: unequal halves),
+    into FP32 scratch in C's head columns; a second kernel adds the halves into the band, and the head grid then
+    overwrites the scratch.  C is a strided view with padding columns and a guard row: every 256x256 tile is
+    checked, nothing outside C changes, and two calls give the same bytes."""
+    fp8q = require_gpu()
+    m, n = 512, 129 * 256
+    kind = "dgrad" if path in ("promoted", "pow2_ab") else "fprop"
+    if path == "promoted":
+        ops = random_fp8_operands(501 + k, m, n, k, kind=kind)
+    else:
+        p2 = random_fp8_operands(501 + k, m, n, k, kind=kind, pow2=True)
+        anyv = random_fp8_operands(501 + k, m, n, k, kind=kind, pow2=False)
+        ops = {"qa": p2["qa"], "qb": p2["qb"], "sa": p2["sa"] if path in ("pow2_a", "pow2_ab") else anyv["sa"],
+               "sb": p2["sb"] if path in ("pow2_b", "pow2_ab") else anyv["sb"]}
+    ref = og.round_bf16(og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind))
+    args = [KINDS[kind]] + [dev(ops[x]) for x in ("qa", "sa", "qb", "sb")]
+    outs = []
+    for _ in range(2):
+        buf = torch.full((m + 1, n + 24), -7.5, dtype=torch.bfloat16, device="cuda")
+        c = buf[:m, :n]
+        if path == "promoted":
+            fp8q.fp8_gemm_blockscaled(*args, c=c)
+        else:
+            mask = {"pow2_a": fp8q.POW2_A, "pow2_b": fp8q.POW2_B, "pow2_ab": fp8q.POW2_AB}[path]
+            fp8q.fp8_gemm_blockscaled_pow2(*args, c=c, pow2_operands=mask)
+        h = host(buf)
+        sentinel = host(torch.tensor([-7.5], dtype=torch.bfloat16))[0]
+        assert np.all(h[m] == sentinel) and np.all(h[:m, n:] == sentinel), "a write landed outside C"
+        outs.append(h[:m, :n].copy())
+    assert np.array_equal(outs[0], outs[1])
+    got = (outs[0].astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    head, tail = slice(0, 128 * 256), slice(128 * 256, n)
+    assert og.rel_frobenius(got[:, head], ref[:, head]) <= TOL
+    assert og.rel_frobenius(got[:, tail], ref[:, tail]) <= TOL
+    # every tile on its own, to a bound that a missing or misplaced tile (error ~1) cannot meet while one BF16
+    # step on a tile's largest entries (about 4e-3 of it) can
+    for r in range(0, m, 256):
+        for cc in range(0, n, 256):
+            t = (slice(r, r + 256), slice(cc, cc + 256))
+            assert og.rel_frobenius(got[t], ref[t]) <= 4e-3, (r, cc)
+
+
 @pytest.mark.parametrize("kind,out,k", [("wgrad", "f32", 384), ("wgrad", "f32acc", 1024),
                                          ("fprop", "f32", 1024), ("fprop", "f32acc", 384)])
 def test_many_tile_fp32_launch_every_tile(kind, out, k):

@@ -146,3 +146,41 @@ def test_counters_derive_mfma_busy_and_wait_split():
     assert (g["wave_issuing"], g["wave_waiting_on_counters"], g["wave_waiting_to_issue"]) == \
         pytest.approx((0.3, 0.3, 0.4))
     assert set(out["gemms"]) == {"gemm Dgrad"}
+
+
+KSPLIT = "void fp8q::gemm_blockscaled_kernel<256, 256, 4, 2, 0, 1, false, 0, 2>(fp8q::GemmArgs)"
+KSUM = "fp8q::(anonymous namespace)::ksplit_sum_bf16_kernel(float const*, long, long, unsigned short*, long, long, long)"
+
+
+def test_a_ksplit_gemm_call_is_one_call_of_three_dispatches():
+    """A BF16 GEMM whose last wave runs with K split in two launches the split grid, the kernel that adds the
+    halves and the grid of the other columns: matched as one call, its three durations summed."""
+    bench = {"kernels": {"quant 1x128+128x1 X": {"us": 50.0}, "gemm Dgrad": {"us": 900.0},
+                         ps.COPY: {"us": 400.0, "outside_step": True}}}
+    rows, t = [], 0
+    did = [0]
+
+    def add(name, dur):
+        nonlocal t
+        did[0] += 1
+        rows.append({"Dispatch_Id": str(did[0]), "Kernel_Name": name, "Start_Timestamp": str(t),
+                     "End_Timestamp": str(t + dur)})
+        t += dur + 10
+
+    for _ in range(3):                       # warm-up 1 + 2 timed steps
+        add(DUAL, 1000)
+        add(KSPLIT, 100000)
+        add(KSUM, 15000)
+        add(GEMM_A, 700000)
+    for _ in range(8):
+        add(COPY, 400000)
+    timed, _ = ps.match(bench, ps.dispatches(rows), 2)
+    assert [len(c) for c in timed["gemm Dgrad"]] == [3, 3]
+    assert ps.dur_us(timed["gemm Dgrad"][0]) == pytest.approx(815.0)
+    assert [len(c) for c in timed["quant 1x128+128x1 X"]] == [1, 1]
+    # the pieces only continue a GEMM call, in their order
+    one = [{"name": GEMM_A}]
+    assert ps.continues_call([{"name": KSPLIT}], KSUM)
+    assert ps.continues_call([{"name": KSPLIT}, {"name": KSUM}], GEMM_A)
+    assert not ps.continues_call(one, GEMM_A) and not ps.continues_call([{"name": DUAL}], KSUM)
+    assert not ps.continues_call([{"name": KSPLIT}, {"name": KSUM}, {"name": GEMM_A}], KSUM)
