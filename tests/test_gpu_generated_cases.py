@@ -190,6 +190,69 @@ def test_generated_gemm(case):
             assert err <= TOL_F32, (r, cc, err)
 
 
+def _draw_wide_cases(rnd=0):
+    """M=512 and N = 256 * nt with nt in 129..192: 2*nt tiles of 256x256, more than the 256 CUs, with a last wave of
+    2..128 tiles in whole 256-column bands, so the launch balances it: as K halves into scratch in C's head columns
+    for BF16 output when the head has room (N_head >= 4 N_tail), else as a grid of 128x256 tiles."""
+    rng = np.random.default_rng(20261206 + 7919 * rnd)
+    cases = []
+    for i in range(6):
+        kind = ["fprop", "dgrad"][i % 2]
+        path = list(PATHS)[(i // 2) % 4]
+        out = ["bf16", "f32"][int(rng.integers(0, 2)) if i >= 2 else 0]
+        nt = int(rng.integers(129, 193))
+        k = 128 * int(rng.integers(2, 11))
+        cases.append((1000 * rnd + i, kind, path, out, 512, 256 * nt, k, (0, 16, 16, 0), (1, 1)))
+    return cases
+
+
+WIDE_CASES = [c for r in range(ROUNDS) for c in _draw_wide_cases(r)]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=_case_id)
+def test_generated_last_wave(case):
+    """Like test_generated_gemm on shapes whose last wave is balanced: the whole output checked against the bar,
+    every 256x256 tile to a bound a missing or misplaced tile cannot meet, FP32 results per tile to the FP32 bar,
+    and nothing outside C written."""
+    fp8q = require_gpu()
+    i, kind, path, out, m, n, k, (a_off, a_pad, b_off, b_pad), (c_off16, c_pad16) = case
+    print(f"generated last-wave case {_case_id(case)}", flush=True)
+    ops = _gemm_operands(9600 + i, kind, path, m, n, k)
+    ref = og.gemm_ref(ops["qa"], ops["sa"], ops["qb"], ops["sb"], kind)
+    abuf, a = _guarded((m, k), torch.uint8, a_off, a_pad, NAN_CODE)
+    bbuf, b = _guarded((n, k), torch.uint8, b_off, b_pad, NAN_CODE)
+    _put(a, ops["qa"])
+    _put(b, ops["qb"])
+    sabuf, sa = _guarded_dense(ops["sa"].shape, 4, float("nan"))
+    sbbuf, sb = _guarded_dense(ops["sb"].shape, 8, float("nan"))
+    _put(sa, ops["sa"])
+    _put(sb, ops["sb"])
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    per16 = 16 // (2 if dt == torch.bfloat16 else 4)
+    c_off, c_pad = per16 * c_off16, per16 * c_pad16
+    cbuf, c = _guarded((m, n), dt, c_off, c_pad, OUT_SENTINEL)
+    args = (KINDS[kind], a, sa, b, sb)
+    if path == "promoted":
+        fp8q.fp8_gemm_blockscaled(*args, c=c)
+    else:
+        fp8q.fp8_gemm_blockscaled_pow2(*args, c=c, pow2_operands=PATHS[path])
+    h = host(cbuf)
+    sent = _sentinel_bits(dt) if dt == torch.bfloat16 else np.float32(OUT_SENTINEL)
+    assert np.all(_outside(h, m, c_off, n) == sent), "a write landed outside C"
+    view = h[:m, c_off:c_off + n]
+    if dt == torch.bfloat16:
+        got = (view.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        want, tol_tile = og.round_bf16(ref), 4e-3
+        assert og.rel_frobenius(got, want) <= TOL
+    else:
+        got, want, tol_tile = view.astype(np.float64), og.round_output(ref, "f32"), TOL_F32
+    assert np.all(np.isfinite(got))
+    for r in range(0, m, 256):
+        for cc in range(0, n, 256):
+            t = (slice(r, r + 256), slice(cc, cc + 256))
+            assert og.rel_frobenius(got[t], want[t]) <= tol_tile, (r, cc)
+
+
 def _draw_grouped_cases(rnd=0):
     rng = np.random.default_rng(20261204 + 7919 * rnd)
     cases = []
