@@ -511,19 +511,24 @@ namespace {
 // The BF16 columns of a GEMM whose K was split in two:
 //   c[m][n] = RNE(p[m][n] + p[m][half + n]),  n < cols,
 // p holding the two FP32 parts side by side in rows of ldp floats.  Eight
-// columns per thread (cols % 8 == 0), 16-byte loads and stores.
-__global__ __launch_bounds__(256) void ksplit_sum_bf16_kernel(const float* __restrict__ p, int64_t ldp, int64_t half,
+// columns per thread (cols % 8 == 0), 16-byte loads and stores; rows
+// blockIdx.y, blockIdx.y + gridDim.y, ...
+__global__ __launch_bounds__(128) void ksplit_sum_bf16_kernel(const float* __restrict__ p, int64_t ldp, int64_t half,
                                                               uint16_t* __restrict__ c, int64_t ldc, int64_t rows,
                                                               int64_t cols) {
-  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
-  if (i >= rows * cols) return;
-  const int64_t m = i / cols, n = i % cols;
-  const v4f* a = reinterpret_cast<const v4f*>(p + m * ldp + n);
-  const v4f* b = reinterpret_cast<const v4f*>(p + m * ldp + half + n);
-  const v4f lo = a[0] + b[0], hi = a[1] + b[1];
-  const u32x4 w = {bf16_rne_bits(lo[0]) | (bf16_rne_bits(lo[1]) << 16), bf16_rne_bits(lo[2]) | (bf16_rne_bits(lo[3]) << 16),
-                   bf16_rne_bits(hi[0]) | (bf16_rne_bits(hi[1]) << 16), bf16_rne_bits(hi[2]) | (bf16_rne_bits(hi[3]) << 16)};
-  *reinterpret_cast<u32x4*>(c + m * ldc + n) = w;
+  const int64_t n = (int64_t(blockIdx.x) * 128 + threadIdx.x) * 8;
+  if (n >= cols) return;
+  for (int64_t m = blockIdx.y; m < rows; m += gridDim.y) {
+    const v4f* a = reinterpret_cast<const v4f*>(p + m * ldp + n);
+    const v4f* b = reinterpret_cast<const v4f*>(p + m * ldp + half + n);
+    const v4f lo = a[0] + b[0], hi = a[1] + b[1];
+    u32x4 w;
+    w.x = bf16_rne_bits(lo[0]) | (bf16_rne_bits(lo[1]) << 16);
+    w.y = bf16_rne_bits(lo[2]) | (bf16_rne_bits(lo[3]) << 16);
+    w.z = bf16_rne_bits(hi[0]) | (bf16_rne_bits(hi[1]) << 16);
+    w.w = bf16_rne_bits(hi[2]) | (bf16_rne_bits(hi[3]) << 16);
+    *reinterpret_cast<u32x4*>(c + m * ldc + n) = w;
+  }
 }
 }  // namespace
 
@@ -604,10 +609,9 @@ static hipError_t launch_balanced(const GemmArgs& a, hipStream_t st) {
             part.split_c_off = rest.N;
             hipError_t e = launch_cfg<256, 256, 4, 2, BSCALE, kOutF32, false, HW, 2>(part, st);
             if (e != hipSuccess) return e;
-            const int64_t threads = a.M * rest.N / 8;
-            hipLaunchKernelGGL(ksplit_sum_bf16_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, st,
-                               static_cast<const float*>(a.c), a.ldc / 2, rest.N, static_cast<uint16_t*>(rest.c),
-                               a.ldc, a.M, rest.N);
+            const dim3 sum_grid(unsigned((rest.N / 8 + 127) / 128), unsigned(a.M < 65535 ? a.M : 65535));
+            hipLaunchKernelGGL(ksplit_sum_bf16_kernel, sum_grid, dim3(128), 0, st, static_cast<const float*>(a.c),
+                               a.ldc / 2, rest.N, static_cast<uint16_t*>(rest.c), a.ldc, a.M, rest.N);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
             return launch_cfg<256, 256, 4, 2, BSCALE, OUT, false, HW>(head, st);
