@@ -79,3 +79,30 @@ def test_pipeline_captured_in_a_hip_graph_and_replayed():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(y_buf), want), seed
+
+
+def test_ksplit_last_wave_captured_in_a_hip_graph_and_replayed():
+    """The same for a GEMM whose half-full last wave runs as K halves (M=512, N=129*256, K=384, BF16 out): the
+    split grid, the kernel adding the halves (both through scratch in C) and the head grid replay in order, and
+    every replay equals the eager result bit for bit."""
+    fp8q = require_gpu()
+    shape = dict(m=512, n=129 * 256, k=384)
+    x_buf, w_buf = _inputs(611, **shape)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _fprop(fp8q, x_buf, w_buf)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y_buf = _fprop(fp8q, x_buf, w_buf)
+    torch.cuda.synchronize()
+    for seed in (621, 622, 623):
+        x, w = _inputs(seed, **shape)
+        want = host(_fprop(fp8q, x, w))
+        x_buf.copy_(x)
+        w_buf.copy_(w)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y_buf), want), seed
