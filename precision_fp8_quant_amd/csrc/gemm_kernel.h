@@ -556,9 +556,10 @@ static hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
 // Balance the last wave of tiles (256 CUs): a 256x256 grid whose last wave
 // is at most half full leaves half the chip idle for a whole tile time.  When
 // those tail tiles form whole 256-column bands (block-scaled B only), the bands
-// run as a second grid of 128x256 tiles -- two per 256x256 tile, one full
-// wave -- right behind the first (e.g. Dgrad 8192x7168: 768 + 256 tiles
-// instead of 896 in 3.5 waves).
+// run either as whole tiles with K split in two (BF16 output, below) or as a
+// second grid of 128x256 tiles -- two per 256x256 tile, one full wave --
+// right behind the first (an 8192x7168 output: 768 + 256 tiles instead of
+// 896 in 3.5 waves).
 template <int BSCALE, int OUT, bool GROUPED, int HW>
 static hipError_t launch_balanced(const GemmArgs& a, hipStream_t st) {
   constexpr int64_t kCUs = 256;
@@ -599,8 +600,9 @@ static hipError_t launch_balanced(const GemmArgs& a, hipStream_t st) {
         // columns of C (which the head grid writes afterwards): the tail runs
         // as whole 256x256 tiles, each as two K halves in one wave of
         // 2 x tail workgroups, into that scratch, and a third kernel adds the
-        // halves into the tail columns.  Otherwise the tail bands run as
-        // 128x256 tiles over the whole K, which read more LDS bytes per MFMA.
+        // halves into the tail columns (Dgrad 8192x7168x18432: 905 -> 860 us).
+        // Otherwise the tail bands run as 128x256 tiles over the whole K,
+        // which read more LDS bytes per MFMA.
         if constexpr (OUT == kOutBF16) {
           if (a.K >= 256 && head.N >= 4 * rest.N) {
             GemmArgs part = rest;
