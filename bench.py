@@ -46,6 +46,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -80,10 +81,16 @@ def parse():
 
 
 def source_hash():
+    """Hash of the device sources with comments and blank space removed: an edit of the kernels' code changes it,
+    an edit of their comments does not (the profiles keyed to it stay valid).  No string literal in these files
+    holds a comment marker."""
     h = hashlib.sha256()
     for f in ("quant.hip", "gemm.hip", "gemm_kernel.h", "gemm_pow2.hip", "fp8q_device.h"):
-        with open(os.path.join(ROOT, "precision_fp8_quant_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "precision_fp8_quant_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -124,3 +124,22 @@ def test_cpu_baseline_records_the_parity_of_every_slice():
     assert lines["gemm Dgrad"]["parity"]["rel_frobenius"] > lines["gemm Dgrad"]["parity"]["bound"]
     tiny = lines["quant 1x128 + 128x128 + Fprop (int64)"]["parity"]
     assert tiny["codes_and_scales"] == "bit-exact" and tiny["ok"] and tiny["rel_frobenius"] == 0.0
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    """The profiles are keyed to the kernels' code: a comment or blank-space edit keeps the hash, a code edit
+    changes it."""
+    import shutil
+    src = os.path.join(ROOT, "precision_fp8_quant_amd", "csrc")
+    dst = tmp_path / "precision_fp8_quant_amd" / "csrc"
+    dst.mkdir(parents=True)
+    for f in ("quant.hip", "gemm.hip", "gemm_kernel.h", "gemm_pow2.hip", "fp8q_device.h"):
+        shutil.copy(os.path.join(src, f), dst / f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.source_hash()
+    k = dst / "gemm_kernel.h"
+    text = k.read_text()
+    k.write_text(text.replace("namespace fp8q {", "namespace fp8q {  // a new comment\n/* and a block\n comment */\n\n", 1))
+    assert bench.source_hash() == h0
+    k.write_text(text.replace("constexpr int64_t kCUs = 256;", "constexpr int64_t kCUs = 255;", 1))
+    assert bench.source_hash() != h0
